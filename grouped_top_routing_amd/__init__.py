@@ -1,0 +1,17 @@
+"""Beam-1.0 mixture-of-experts block on one AMD Instinct MI355X (gfx950).
+
+The block ("Welcome Beam: a 501B open model you can own, customize, and
+scale", section "Mixture of Experts"): FP32 router GEMM, sigmoid scores,
+group-limited top-8 selection (8 groups of 32, 4 groups kept by the sum of
+their two best scores), token permutation, bf16 SwiGLU expert grouped GEMMs
+and a weighted combine scaled by 2.5, with no shared expert.
+
+All computation happens in the HIP kernels of ``libbeam_moe.so`` (C ABI in
+include/beam_moe.h); this package only marshals torch tensors into it.
+"""
+from ._lib import (  # noqa: F401
+    ENTRY_EXPERT_FFN, ENTRY_EXPERT_STAGE, ENTRY_LAYER, ENTRY_PERMUTE, ENTRY_ROUTE, EXPORTS,
+    LIB_PATH, MoeConfig, MoeError, Workspace, combine, expert_down, expert_ffn, expert_gate_up,
+    layer_forward, lib, make_config, permute, route, route_replay, status_string,
+    workspace_bytes,
+)

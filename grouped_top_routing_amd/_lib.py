@@ -1,0 +1,315 @@
+"""ctypes binding of libbeam_moe.so (argument marshalling only).
+
+Every step of the MoE block runs in the library's HIP kernels; this module
+checks tensor dtypes, shapes and devices, allocates outputs and the workspace
+with torch, and passes raw device pointers plus the current HIP stream.  There
+is no fallback: if the library is missing or a call fails, it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbeam_moe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+ENTRY_ROUTE = 0
+ENTRY_PERMUTE = 1
+ENTRY_EXPERT_FFN = 2
+ENTRY_LAYER = 3
+ENTRY_EXPERT_STAGE = 4
+
+#: Every symbol include/beam_moe.h declares.
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_replay", "moe_permute",
+           "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
+           "moe_layer_forward", "moe_status_string")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("hidden", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("topk_groups", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("renormalize", ctypes.c_int32),
+        ("routed_scaling", ctypes.c_float),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m grouped_top_routing_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        CP = ctypes.POINTER(MoeConfig)
+        L.moe_workspace_bytes.argtypes = [CP, I, ctypes.POINTER(Z)]
+        L.moe_route.argtypes = [CP, P, P, P, P, P, P, Z, P]
+        L.moe_route_replay.argtypes = [CP, P, P, P, P, P, Z, P]
+        L.moe_permute.argtypes = [CP, P, P, P, P, P, P, Z, P]
+        L.moe_expert_ffn.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
+        L.moe_expert_gate_up.argtypes = [CP, P, P, P, P, P, P, Z, P]
+        L.moe_expert_down.argtypes = [CP, P, P, P, P, P, Z, P]
+        L.moe_combine.argtypes = [CP, P, P, P, P, P]
+        L.moe_layer_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
+        L.moe_status_string.argtypes = [I]
+        L.moe_status_string.restype = ctypes.c_char_p
+        for name in EXPORTS:
+            if name != "moe_status_string":
+                getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().moe_status_string(int(code)).decode()
+
+
+def make_config(num_tokens, hidden, intermediate, *, num_experts=256, num_groups=8,
+                topk_groups=4, topk=8, renormalize=True, routed_scaling=2.5) -> MoeConfig:
+    return MoeConfig(int(num_tokens), int(hidden), int(intermediate), int(num_experts),
+                     int(num_groups), int(topk_groups), int(topk), int(bool(renormalize)),
+                     float(routed_scaling))
+
+
+def workspace_bytes(cfg: MoeConfig, entry: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().moe_workspace_bytes(ctypes.byref(cfg), int(entry), ctypes.byref(n))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_workspace_bytes")
+    return int(n.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class Workspace:
+    """A reusable device workspace (a torch uint8 buffer grown on demand)."""
+
+    def __init__(self):
+        self._buf = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        if self._buf is None or self._buf.numel() < nbytes or self._buf.device != device:
+            self._buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self._buf
+
+
+_default_ws: dict = {}
+
+
+def _ws(workspace, device):
+    if workspace is None:
+        workspace = _default_ws.setdefault(device, Workspace())
+    return workspace
+
+
+def _call(name, code):
+    if code != MOE_OK:
+        raise MoeError(code, name)
+
+
+def route(x, w_router, *, sel_bias=None, num_groups=8, topk_groups=4, topk=8, renormalize=True,
+          workspace=None):
+    """Router: returns (topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check(x, "x", torch.bfloat16)
+    _check(w_router, "w_router", torch.float32, (E, H), x.device)
+    if sel_bias is not None:
+        _check(sel_bias, "sel_bias", torch.float32, (E,), x.device)
+    cfg = make_config(T, H, 128, num_experts=E, num_groups=num_groups, topk_groups=topk_groups,
+                      topk=topk, renormalize=renormalize)
+    ids = torch.empty(T, topk, dtype=torch.int32, device=x.device)
+    w = torch.empty(T, topk, dtype=torch.float32, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_ROUTE)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_route", lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(sel_bias),
+                                       _ptr(ids), _ptr(w), _ptr(ws), nb, _stream(x.device)))
+    return ids, w
+
+
+def route_replay(x, w_router, topk_ids, *, renormalize=True, workspace=None):
+    """Combine weights for caller-supplied expert ids: fp32 [T, k]."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    k = topk_ids.shape[1]
+    _check(x, "x", torch.bfloat16)
+    _check(w_router, "w_router", torch.float32, (E, H), x.device)
+    _check(topk_ids, "topk_ids", torch.int32, (T, k), x.device)
+    cfg = make_config(T, H, 128, num_experts=E, num_groups=1, topk_groups=1, topk=k,
+                      renormalize=renormalize)
+    w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_ROUTE)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_route_replay", lib().moe_route_replay(ctypes.byref(cfg), _ptr(x), _ptr(w_router),
+                                                     _ptr(topk_ids), _ptr(w), _ptr(ws), nb,
+                                                     _stream(x.device)))
+    return w
+
+
+def permute(topk_ids, *, num_experts=256, workspace=None):
+    """Returns (counts [E], offsets [E+1], perm_src [T*k], perm_dst [T*k]), all int32."""
+    T, k = topk_ids.shape
+    _check(topk_ids, "topk_ids", torch.int32)
+    dev = topk_ids.device
+    cfg = make_config(T, 256, 128, num_experts=num_experts, num_groups=1, topk_groups=1, topk=k)
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    psrc = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pdst = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nb = workspace_bytes(cfg, ENTRY_PERMUTE)
+    ws = _ws(workspace, dev).get(nb, dev)
+    _call("moe_permute", lib().moe_permute(ctypes.byref(cfg), _ptr(topk_ids), _ptr(counts),
+                                           _ptr(offsets), _ptr(psrc), _ptr(pdst), _ptr(ws), nb,
+                                           _stream(dev)))
+    return counts, offsets, psrc, pdst
+
+
+def expert_ffn(x, perm_src, offsets, w_gate_up, w_down, *, topk=8, workspace=None):
+    """Expert SwiGLU MLPs over the permuted rows: y_perm bf16 [T*k, H]."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    _check(x, "x", torch.bfloat16)
+    _check(perm_src, "perm_src", torch.int32, (T * topk,), x.device)
+    _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk)
+    y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_FFN)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_expert_ffn", lib().moe_expert_ffn(ctypes.byref(cfg), _ptr(x), _ptr(perm_src),
+                                                 _ptr(offsets), _ptr(w_gate_up), _ptr(w_down),
+                                                 _ptr(y), _ptr(ws), nb, _stream(x.device)))
+    return y
+
+
+def expert_gate_up(x, perm_src, offsets, w_gate_up, *, topk=8, workspace=None):
+    """First expert GEMM with the fused SwiGLU: h bf16 [T*k, I]."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    _check(x, "x", torch.bfloat16)
+    _check(perm_src, "perm_src", torch.int32, (T * topk,), x.device)
+    _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk)
+    h = torch.empty(T * topk, I, dtype=torch.bfloat16, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_STAGE)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_expert_gate_up", lib().moe_expert_gate_up(
+        ctypes.byref(cfg), _ptr(x), _ptr(perm_src), _ptr(offsets), _ptr(w_gate_up), _ptr(h),
+        _ptr(ws), nb, _stream(x.device)))
+    return h
+
+
+def expert_down(h, offsets, w_down, *, topk=8, workspace=None):
+    """Second expert GEMM: y_perm bf16 [T*k, H]."""
+    R, I = h.shape
+    E, H, _ = w_down.shape
+    T = R // topk
+    _check(h, "h", torch.bfloat16, (T * topk, I))
+    _check(offsets, "offsets", torch.int32, (E + 1,), h.device)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), h.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk)
+    y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=h.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_STAGE)
+    ws = _ws(workspace, h.device).get(nb, h.device)
+    _call("moe_expert_down", lib().moe_expert_down(
+        ctypes.byref(cfg), _ptr(h), _ptr(offsets), _ptr(w_down), _ptr(y), _ptr(ws), nb,
+        _stream(h.device)))
+    return y
+
+
+def combine(y_perm, perm_dst, topk_w, *, routed_scaling=2.5):
+    """Weighted un-permute: out bf16 [T, H]."""
+    T, k = topk_w.shape
+    H = y_perm.shape[1]
+    _check(y_perm, "y_perm", torch.bfloat16)
+    _check(perm_dst, "perm_dst", torch.int32, (T * k,), y_perm.device)
+    _check(topk_w, "topk_w", torch.float32, (T, k), y_perm.device)
+    cfg = make_config(T, H, 128, num_groups=1, topk_groups=1, topk=k,
+                      routed_scaling=routed_scaling)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=y_perm.device)
+    _call("moe_combine", lib().moe_combine(ctypes.byref(cfg), _ptr(y_perm), _ptr(perm_dst),
+                                           _ptr(topk_w), _ptr(out), _stream(y_perm.device)))
+    return out
+
+
+def layer_forward(x, w_router, w_gate_up, w_down, *, sel_bias=None, num_groups=8, topk_groups=4,
+                  topk=8, renormalize=True, routed_scaling=2.5, return_routing=False,
+                  out=None, workspace=None):
+    """The whole MoE block.  Returns out bf16 [T, H] (and (ids, w) if asked)."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    _check(x, "x", torch.bfloat16)
+    _check(w_router, "w_router", torch.float32, (E, H), x.device)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), x.device)
+    if sel_bias is not None:
+        _check(sel_bias, "sel_bias", torch.float32, (E,), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=num_groups, topk_groups=topk_groups,
+                      topk=topk, renormalize=renormalize, routed_scaling=routed_scaling)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    else:
+        _check(out, "out", torch.bfloat16, (T, H), x.device)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty(T, topk, dtype=torch.int32, device=x.device)
+        w = torch.empty(T, topk, dtype=torch.float32, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_LAYER)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_layer_forward",
+          lib().moe_layer_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(sel_bias),
+                                  _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(ids), _ptr(w),
+                                  _ptr(ws), nb, _stream(x.device)))
+    return (out, ids, w) if return_routing else out

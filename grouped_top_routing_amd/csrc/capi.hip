@@ -1,0 +1,362 @@
+// C ABI of the MoE block: argument validation, workspace carving and launch
+// sequencing.  Declarations and the contract of every entry point are in
+// include/beam_moe.h.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/beam_moe.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace beam;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int validate(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens < 0 || c->hidden <= 0 || c->intermediate <= 0 || c->num_experts <= 0 ||
+      c->num_groups <= 0 || c->topk_groups <= 0 || c->topk <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->routed_scaling)) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts % c->num_groups != 0) return MOE_ERR_INVALID_ARG;
+  if (c->topk_groups > c->num_groups) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)c->topk > (int64_t)c->topk_groups * (c->num_experts / c->num_groups))
+    return MOE_ERR_INVALID_ARG;
+  // shapes the gfx950 kernels are built for
+  if (c->num_experts != 256) return MOE_ERR_UNSUPPORTED;
+  if (c->num_groups > 64 || (c->num_groups & (c->num_groups - 1)) != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->topk > 8) return MOE_ERR_UNSUPPORTED;
+  if (c->hidden % 256 != 0 || c->intermediate % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->num_tokens * (int64_t)c->topk >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t pairs(const moe_config_t* c) { return c->num_tokens * (int64_t)c->topk; }
+
+int mb_for(const moe_config_t* c) { return ffn_choose_mb(pairs(c), c->num_experts); }
+
+int64_t max_tiles_for(const moe_config_t* c) {
+  const int64_t n = pairs(c);
+  const int64_t bmax = ffn_rows_per_tile(mb_for(c));
+  return n / bmax + (n < c->num_experts ? n : c->num_experts) + 1;
+}
+
+size_t route_ws(const moe_config_t* c) {
+  return align_up((size_t)c->num_tokens * c->num_experts * sizeof(float));
+}
+size_t permute_ws(const moe_config_t* c) {
+  const int64_t nchunks = (pairs(c) + kChunk - 1) / kChunk;
+  return align_up((size_t)(nchunks > 0 ? nchunks : 1) * c->num_experts * sizeof(int32_t));
+}
+size_t plan_bytes(const moe_config_t* c) {
+  return align_up((size_t)(4 + 3 * max_tiles_for(c)) * sizeof(int32_t));
+}
+size_t ffn_ws(const moe_config_t* c) {
+  return plan_bytes(c) + align_up((size_t)pairs(c) * c->intermediate * sizeof(uint16_t));
+}
+
+struct LayerLayout {
+  size_t ids, w, counts, offsets, psrc, pdst, y, scratch, total;
+};
+
+LayerLayout layer_layout(const moe_config_t* c) {
+  LayerLayout L{};
+  const size_t n = (size_t)pairs(c);
+  size_t o = 0;
+  L.ids = o;      o += align_up(n * sizeof(int32_t));
+  L.w = o;        o += align_up(n * sizeof(float));
+  L.counts = o;   o += align_up((size_t)c->num_experts * sizeof(int32_t));
+  L.offsets = o;  o += align_up((size_t)(c->num_experts + 1) * sizeof(int32_t));
+  L.psrc = o;     o += align_up(n * sizeof(int32_t));
+  L.pdst = o;     o += align_up(n * sizeof(int32_t));
+  L.y = o;        o += align_up(n * (size_t)c->hidden * sizeof(uint16_t));
+  L.scratch = o;
+  size_t s = route_ws(c);
+  if (permute_ws(c) > s) s = permute_ws(c);
+  if (ffn_ws(c) > s) s = ffn_ws(c);
+  o += s;
+  L.total = o;
+  return L;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws || have < need) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int device_ready() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Persistent grid for the grouped GEMM: all CUs, 2 workgroups each (a
+// multiple of 8 so every XCD gets the same number of workgroups).
+int gemm_grid(int64_t max_items) {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int n = 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (dev < 64) n = cus[dev];
+    if (n == 0) {
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+      if (dev < 64) cus[dev] = n;
+    }
+  }
+  int64_t grid = (int64_t)n * 2;
+  const int64_t cap = (max_items + 7) / 8 * 8;
+  if (cap < grid) grid = cap;
+  grid = (grid + 7) / 8 * 8;
+  return (int)(grid > 0 ? grid : 8);
+}
+
+// ---- internal steps (arguments already validated) ----
+int do_route(const moe_config_t* c, const uint16_t* x, const float* wr, const float* bias,
+             int32_t* ids, float* w, void* scratch, hipStream_t s) {
+  const int T = (int)c->num_tokens;
+  float* logits = static_cast<float*>(scratch);
+  int st = hip_status(launch_router_logits(x, wr, logits, T, c->hidden, c->num_experts, s));
+  if (st) return st;
+  return hip_status(launch_select(logits, bias, ids, w, T, c->num_groups, c->topk_groups, c->topk,
+                                  c->renormalize, s));
+}
+
+int do_permute(const moe_config_t* c, const int32_t* ids, int32_t* counts, int32_t* offsets,
+               int32_t* psrc, int32_t* pdst, void* scratch, hipStream_t s) {
+  return hip_status(launch_permute(ids, pairs(c), c->num_experts, counts, offsets, psrc, pdst,
+                                   static_cast<int32_t*>(scratch), s));
+}
+
+int do_plan(const moe_config_t* c, const int32_t* offsets, int32_t* plan, hipStream_t s) {
+  return hip_status(launch_tile_plan(offsets, c->num_experts, ffn_rows_per_tile(mb_for(c)), plan,
+                                     (int)max_tiles_for(c), s));
+}
+
+int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
+               const int32_t* plan, const uint16_t* wgu, uint16_t* h, hipStream_t s) {
+  const int64_t max_tiles = max_tiles_for(c);
+  const int H = c->hidden, I = c->intermediate;
+  const int grid = gemm_grid(max_tiles * (I / ffn_out_cols_per_item(true)));
+  if (grid < 0) return MOE_ERR_HIP;
+  return hip_status(launch_grouped_gemm(mb_for(c), true, x, psrc, c->topk, wgu,
+                                        (int64_t)2 * I * H, h, plan, (int)max_tiles, H, I, I,
+                                        grid, s));
+}
+
+int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint16_t* wd,
+            uint16_t* y, hipStream_t s) {
+  const int64_t max_tiles = max_tiles_for(c);
+  const int H = c->hidden, I = c->intermediate;
+  const int grid = gemm_grid(max_tiles * (H / ffn_out_cols_per_item(false)));
+  if (grid < 0) return MOE_ERR_HIP;
+  return hip_status(launch_grouped_gemm(mb_for(c), false, h, nullptr, c->topk, wd,
+                                        (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0, grid,
+                                        s));
+}
+
+int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const int32_t* offsets,
+           const uint16_t* wgu, const uint16_t* wd, uint16_t* y, void* scratch, hipStream_t s) {
+  int32_t* plan = static_cast<int32_t*>(scratch);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + plan_bytes(c));
+  int st = do_plan(c, offsets, plan, s);
+  if (st) return st;
+  if ((st = do_gate_up(c, x, psrc, plan, wgu, h, s))) return st;
+  return do_down(c, h, plan, wd, y, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by the gfx950 kernels";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_workspace_bytes(const moe_config_t* cfg, int entry, size_t* bytes) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  switch (entry) {
+    case MOE_ENTRY_ROUTE: *bytes = route_ws(cfg); break;
+    case MOE_ENTRY_PERMUTE: *bytes = permute_ws(cfg); break;
+    case MOE_ENTRY_EXPERT_FFN: *bytes = ffn_ws(cfg); break;
+    case MOE_ENTRY_LAYER: *bytes = layer_layout(cfg).total; break;
+    case MOE_ENTRY_EXPERT_STAGE: *bytes = plan_bytes(cfg); break;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int moe_route(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+              const float* sel_bias, int32_t* topk_ids, float* topk_w, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w) ||
+      (sel_bias && !aligned4(sel_bias)))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, route_ws(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  return do_route(cfg, x, w_router, sel_bias, topk_ids, topk_w, workspace,
+                  static_cast<hipStream_t>(stream));
+}
+
+int moe_route_replay(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                     const int32_t* topk_ids, float* topk_w, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, route_ws(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = static_cast<float*>(workspace);
+  const int T = (int)cfg->num_tokens;
+  st = hip_status(launch_router_logits(x, w_router, logits, T, cfg->hidden, cfg->num_experts, s));
+  if (st) return st;
+  return hip_status(
+      launch_replay(logits, topk_ids, topk_w, T, cfg->num_experts, cfg->topk, cfg->renormalize, s));
+}
+
+int moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts,
+                int32_t* offsets, int32_t* perm_src, int32_t* perm_dst, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!topk_ids || !counts || !offsets || !perm_src || !perm_dst) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(topk_ids) || !aligned4(counts) || !aligned4(offsets) || !aligned4(perm_src) ||
+      !aligned4(perm_dst))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, permute_ws(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  return do_permute(cfg, topk_ids, counts, offsets, perm_src, perm_dst, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                   const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
+                   uint16_t* y_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!x || !perm_src || !offsets || !w_gate_up || !w_down || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y_perm) ||
+      !aligned4(perm_src) || !aligned4(offsets))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, ffn_ws(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  return do_ffn(cfg, x, perm_src, offsets, w_gate_up, w_down, y_perm, workspace,
+                static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_gate_up(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                       const int32_t* offsets, const uint16_t* w_gate_up, uint16_t* h,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!x || !perm_src || !offsets || !w_gate_up || !h) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(h) || !aligned4(perm_src) ||
+      !aligned4(offsets))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, plan_bytes(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* plan = static_cast<int32_t*>(workspace);
+  if ((st = do_plan(cfg, offsets, plan, s))) return st;
+  return do_gate_up(cfg, x, perm_src, plan, w_gate_up, h, s);
+}
+
+int moe_expert_down(const moe_config_t* cfg, const uint16_t* h, const int32_t* offsets,
+                    const uint16_t* w_down, uint16_t* y_perm, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!h || !offsets || !w_down || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(y_perm) || !aligned4(offsets))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, plan_bytes(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* plan = static_cast<int32_t*>(workspace);
+  if ((st = do_plan(cfg, offsets, plan, s))) return st;
+  return do_down(cfg, h, plan, w_down, y_perm, s);
+}
+
+int moe_combine(const moe_config_t* cfg, const uint16_t* y_perm, const int32_t* perm_dst,
+                const float* topk_w, uint16_t* out, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!y_perm || !perm_dst || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(out) || !aligned4(perm_dst) || !aligned4(topk_w))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  return hip_status(launch_combine(y_perm, perm_dst, topk_w, out, (int)cfg->num_tokens,
+                                   cfg->hidden, cfg->topk, cfg->routed_scaling,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                      const float* sel_bias, const uint16_t* w_gate_up, const uint16_t* w_down,
+                      uint16_t* out, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!x || !w_router || !w_gate_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate_up) || !aligned16(w_down) ||
+      !aligned16(out) || (sel_bias && !aligned4(sel_bias)) ||
+      (topk_ids_out && !aligned4(topk_ids_out)) || (topk_w_out && !aligned4(topk_w_out)))
+    return MOE_ERR_INVALID_ARG;
+  const LayerLayout L = layer_layout(cfg);
+  if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* psrc = reinterpret_cast<int32_t*>(ws + L.psrc);
+  int32_t* pdst = reinterpret_cast<int32_t*>(ws + L.pdst);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+  void* scratch = ws + L.scratch;
+  if ((st = do_route(cfg, x, w_router, sel_bias, ids, w, scratch, s))) return st;
+  if ((st = do_permute(cfg, ids, counts, offsets, psrc, pdst, scratch, s))) return st;
+  if ((st = do_ffn(cfg, x, psrc, offsets, w_gate_up, w_down, y, scratch, s))) return st;
+  return hip_status(launch_combine(y, pdst, w, out, (int)cfg->num_tokens, cfg->hidden, cfg->topk,
+                                   cfg->routed_scaling, s));
+}
+
+}  // extern "C"

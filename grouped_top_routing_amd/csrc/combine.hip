@@ -1,0 +1,58 @@
+// Weighted un-permute of the Beam-1.0 MoE block on gfx950.
+//
+// "Welcome Beam: a 501B open model you can own, customize, and scale", section
+// "Mixture of Experts": the chosen experts' outputs are combined with the
+// normalized router weights and scaled by 2.5; there is no shared expert.
+//
+// out[t, :] = bf16( scale * sum_j w[t, j] * y[perm_dst[t*topk + j], :] ), the
+// sum taken in fp32 in slot order.  One workgroup per token; every thread
+// owns 8 consecutive columns, so each of the token's rows is read with
+// coalesced 16-byte loads and the output row is written the same way.
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ perm_dst,
+                                                      const float* __restrict__ w,
+                                                      uint16_t* __restrict__ out, int H, int topk,
+                                                      float scale) {
+  const int t = blockIdx.x;
+  int rows[8];
+  float wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = j < topk ? perm_dst[(size_t)t * topk + j] : -1;
+    wt[j] = j < topk ? w[(size_t)t * topk + j] : 0.f;
+  }
+  for (int v = threadIdx.x; v < H / 8; v += blockDim.x) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (rows[j] >= 0) {
+        const uint4 q = ld16(y + (size_t)rows[j] * H + 8 * v);
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * c] += wt[j] * bf16_to_f32(u[c] & 0xffffu);
+          acc[2 * c + 1] += wt[j] * bf16_to_f32(u[c] >> 16);
+        }
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      o[c] = f32_to_bf16(scale * acc[2 * c]) | (f32_to_bf16(scale * acc[2 * c + 1]) << 16);
+    st16(out + (size_t)t * H + 8 * v, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+}
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
+                          uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(128), 0, stream, y, perm_dst, w, out, H, topk,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,36 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+constexpr int kChunk = 4096;  // (token, slot) pairs per permute workgroup
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* logits, int T, int H,
+                                int E, hipStream_t stream);
+hipError_t launch_select(const float* logits, const float* sel_bias, int32_t* ids, float* w,
+                         int T, int G, int topk_groups, int topk, int renormalize,
+                         hipStream_t stream);
+hipError_t launch_replay(const float* logits, const int32_t* ids, float* w, int T, int E,
+                         int topk, int renormalize, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_src, int32_t* perm_dst, int32_t* chunk_hist,
+                          hipStream_t stream);
+
+int ffn_choose_mb(int64_t rows, int E);
+int ffn_rows_per_tile(int mb);
+int ffn_out_cols_per_item(bool swiglu);
+hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* plan, int max_tiles,
+                            hipStream_t stream);
+hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
+                               int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
+                               const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
+                               int grid, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
+                          uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream);
+
+}  // namespace beam

@@ -1,0 +1,181 @@
+/*
+ * beam_moe.h -- C ABI of the Beam-1.0 mixture-of-experts block on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The block ("Welcome Beam: a 501B open model you can own, customize, and
+ * scale", section "Mixture of Experts"; "Beam 1.0" miles recipes, section 1
+ * "Model Introduction"):
+ *   1. router GEMM in FP32 (router weights are kept in FP32; the same page's
+ *      section "Residual Stream" lists the router among the FP32 computations),
+ *   2. sigmoid score for every expert,
+ *   3. experts split into num_groups contiguous groups; each group scored by the
+ *      sum of its two best scores; the topk_groups best groups are kept,
+ *   4. the topk best experts inside the kept groups are chosen,
+ *   5. each chosen expert is a SwiGLU MLP (gate/up projection, SiLU(gate)*up
+ *      in FP32, down projection), with no shared expert,
+ *   6. expert outputs are combined with the normalized router weights and
+ *      scaled by routed_scaling (2.5).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory; scratch space comes from the
+ *     caller's workspace (size from moe_workspace_bytes).
+ *   - bf16 tensors are passed as uint16_t bit patterns.  All tensors are dense
+ *     row-major with the layouts stated per argument.  Tensor pointers and the
+ *     workspace must be 16-byte aligned.
+ *   - Every call validates its arguments on the host first.  On any error it
+ *     enqueues nothing and returns a negative status; MOE_OK (0) otherwise.
+ *     num_tokens == 0 is a valid no-op.  A failed kernel launch returns
+ *     MOE_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation of `stream`.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call never synchronises it.  Calls that share a workspace must be
+ *     ordered on one stream.
+ *   - Results are bitwise deterministic: no floating-point atomics.
+ *   - Supported shapes: num_experts == 256; num_groups a power of two in
+ *     [1, 64]; 1 <= topk_groups <= num_groups; 1 <= topk <= 8 and topk not
+ *     above the experts in the kept groups; hidden a multiple of 256;
+ *     intermediate a multiple of 128; num_tokens * topk < 2^31.  Other shapes return
+ *     MOE_ERR_UNSUPPORTED.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative size, misalignment     */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside the shapes listed above     */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required    */
+  MOE_ERR_HIP = -4           /* HIP runtime error (no device, launch failure) */
+};
+
+/* Which entry point a workspace size is asked for. */
+enum moe_entry {
+  MOE_ENTRY_ROUTE = 0,
+  MOE_ENTRY_PERMUTE = 1,
+  MOE_ENTRY_EXPERT_FFN = 2,
+  MOE_ENTRY_LAYER = 3,
+  MOE_ENTRY_EXPERT_STAGE = 4  /* moe_expert_gate_up or moe_expert_down */
+};
+
+typedef struct moe_config {
+  int64_t num_tokens;     /* T >= 0 tokens in this call                           */
+  int32_t hidden;         /* H: 5120 for Beam-1.0                                 */
+  int32_t intermediate;   /* I: SwiGLU intermediate size, 2560 for Beam-1.0       */
+  int32_t num_experts;    /* E = 256                                              */
+  int32_t num_groups;     /* G = 8 groups of E/G contiguous experts               */
+  int32_t topk_groups;    /* groups kept per token, 4                             */
+  int32_t topk;           /* experts per token, 8                                 */
+  int32_t renormalize;    /* 1: combine weight = score / sum of the topk chosen
+                             scores ("normalized router weights"); 0: raw score   */
+  float routed_scaling;   /* factor applied to the combined output, 2.5          */
+} moe_config_t;
+
+/* Bytes of workspace `entry` needs for `cfg` (written to *bytes). */
+int moe_workspace_bytes(const moe_config_t* cfg, int entry, size_t* bytes);
+
+/*
+ * Router: logits = x . W_r^T in FP32 (bf16 inputs widened exactly), scores =
+ * sigmoid(logits), group-limited top-k selection, combine weights.
+ *   x         [T, H] bf16
+ *   w_router  [E, H] fp32, one row per expert
+ *   sel_bias  [E] fp32 or NULL: added to the scores for choosing only (the
+ *             checkpoint's FP32 "expert biases" read as a selection bias); the
+ *             combine weights always use the unbiased scores
+ *   topk_ids  [T, topk] int32 out, ordered by (selection value desc, id asc)
+ *   topk_w    [T, topk] fp32 out, combine weights WITHOUT routed_scaling
+ * Ties between equal values go to the lower group / expert index.
+ */
+int moe_route(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+              const float* sel_bias, int32_t* topk_ids, float* topk_w,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Routing replay: recompute scores and combine weights for caller-supplied
+ * expert ids (e.g. recorded at rollout time), skipping selection.
+ *   topk_ids  [T, topk] int32 in, each in [0, E)
+ *   topk_w    [T, topk] fp32 out
+ */
+int moe_route_replay(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                     const int32_t* topk_ids, float* topk_w,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Token permutation and per-expert histogram (stable counting sort of the
+ * T*topk (token, slot) pairs by expert).
+ *   topk_ids  [T, topk] int32 in; ids outside [0, E) are dropped (their
+ *             perm_dst entry is -1 and they are not counted)
+ *   counts    [E] int32 out: pairs routed to each expert
+ *   offsets   [E + 1] int32 out: exclusive prefix sum of counts
+ *   perm_src  [T*topk] int32 out: row r of the expert-major order holds pair
+ *             perm_src[r] = t*topk + j; rows of one expert ascend in t
+ *   perm_dst  [T*topk] int32 out: inverse, perm_dst[t*topk + j] = r
+ */
+int moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts,
+                int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Expert SwiGLU MLPs over the permuted rows (bf16 grouped GEMMs with FP32
+ * accumulation; SiLU(gate)*up in FP32, rounded to bf16 before the down GEMM).
+ *   x          [T, H] bf16; row r reads token perm_src[r] / topk
+ *   perm_src   [T*topk] int32, offsets [E + 1] int32 (from moe_permute)
+ *   w_gate_up  [E, 2*I, H] bf16: rows [0, I) gate, rows [I, 2I) up
+ *   w_down     [E, H, I] bf16
+ *   y_perm     [T*topk, H] bf16 out, expert-major row order
+ * Experts with no rows read no weights.
+ */
+int moe_expert_ffn(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                   const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
+                   uint16_t* y_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of moe_expert_ffn, for callers that time or schedule them
+ * separately (same kernels, same results).
+ *   moe_expert_gate_up: h [T*topk, I] bf16 out = bf16(SiLU(x_r . Wg^T) * (x_r . Wu^T))
+ *   moe_expert_down:    y_perm [T*topk, H] bf16 out = bf16(h_r . Wd^T)
+ * Each builds its own m-tile plan from `offsets` in its workspace
+ * (moe_workspace_bytes with MOE_ENTRY_EXPERT_STAGE).
+ */
+int moe_expert_gate_up(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                       const int32_t* offsets, const uint16_t* w_gate_up, uint16_t* h,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int moe_expert_down(const moe_config_t* cfg, const uint16_t* h, const int32_t* offsets,
+                    const uint16_t* w_down, uint16_t* y_perm,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Weighted un-permute: out[t] = bf16(routed_scaling * sum_j topk_w[t, j] *
+ * y_perm[perm_dst[t*topk + j]]), summed in FP32 in slot order.  Slots with
+ * perm_dst < 0 contribute nothing.
+ *   out  [T, H] bf16 out
+ */
+int moe_combine(const moe_config_t* cfg, const uint16_t* y_perm, const int32_t* perm_dst,
+                const float* topk_w, uint16_t* out, void* stream);
+
+/*
+ * The whole block: route, permute, expert MLPs, combine.
+ *   out           [T, H] bf16 out
+ *   topk_ids_out  [T, topk] int32 out or NULL
+ *   topk_w_out    [T, topk] fp32 out or NULL
+ */
+int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                      const float* sel_bias, const uint16_t* w_gate_up, const uint16_t* w_down,
+                      uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

@@ -1,0 +1,69 @@
+"""Helpers shared by the GPU parity tests (test infrastructure only)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+#: Layer-output tolerance: max |y - r| / max(|r|, RMS(r)) and mean |y - r| / RMS(r).
+MAX_REL = 2e-2
+MEAN_REL = 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def err_stats(y, r):
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    if r.size == 0 or rms == 0.0:
+        return 0.0, 0.0, rms
+    d = np.abs(y - r)
+    return float(np.max(d / np.maximum(np.abs(r), rms))), float(np.mean(d) / rms), rms
+
+
+def assert_close(y, r, what, max_rel=MAX_REL, mean_rel=MEAN_REL):
+    mx, mn, rms = err_stats(y, r)
+    say(f"  {what}: max_rel={mx:.3e} mean_rel={mn:.3e} rms={rms:.3e}")
+    assert mx <= max_rel, f"{what}: max relative error {mx:.3e} > {max_rel}"
+    assert mn <= mean_rel, f"{what}: mean abs error {mn:.3e} > {mean_rel} * RMS"
+
+
+def to_np(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def check_routing(ids_gpu, w_gpu, rr, *, n_groups=8, topk_groups=4, topk=8, w_rtol=1e-5):
+    """Routing parity: chosen-expert sets bit-exact for tokens whose oracle
+    margin is at least MARGIN_TOL; flagged tokens must be admissible.  Sets are
+    compared (the order inside a set follows values that may sit closer than
+    fp32 rounding); weights are compared expert by expert.  Returns
+    (n_flagged, n_flagged_differing)."""
+    ids_gpu = np.asarray(ids_gpu).astype(np.int64)
+    w_gpu = np.asarray(w_gpu, dtype=np.float64)
+    flagged = rr.margin < oracle.MARGIN_TOL
+    ok = ~flagged
+    og, oo = np.argsort(ids_gpu, axis=1), np.argsort(rr.ids, axis=1)
+    ids_gpu = np.take_along_axis(ids_gpu, og, 1)
+    w_gpu = np.take_along_axis(w_gpu, og, 1)
+    ids_ref = np.take_along_axis(rr.ids, oo, 1)
+    w_ref = np.take_along_axis(rr.weights, oo, 1)
+    same = np.all(ids_gpu == ids_ref, axis=1)
+    bad = np.nonzero(ok & ~same)[0]
+    assert bad.size == 0, f"{bad.size} unflagged tokens differ, first {bad[:5]}: " \
+                          f"gpu {ids_gpu[bad[0]]} oracle {ids_ref[bad[0]]} margin {rr.margin[bad[0]]}"
+    for t in np.nonzero(flagged & ~same)[0]:
+        assert oracle.selection_admissible(rr.sel[t], rr.group_scores[t], ids_gpu[t],
+                                           n_groups=n_groups, topk_groups=topk_groups,
+                                           topk=topk), f"token {t}: inadmissible {ids_gpu[t]}"
+    m = ok | same
+    np.testing.assert_allclose(w_gpu[m], w_ref[m], rtol=w_rtol, atol=1e-7)
+    return int(flagged.sum()), int((flagged & ~same).sum())

@@ -1,0 +1,139 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_top_routing_amd as gtr
+from grouped_top_routing_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "beam_moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gtr.lib()
+    declared = _declared_symbols()
+    assert declared == sorted(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert gtr.status_string(code).startswith("MOE_")
+    assert "unknown" in gtr.status_string(7)
+
+
+def _cfg(**kw):
+    base = dict(num_tokens=64, hidden=256, intermediate=128)
+    base.update(kw)
+    return gtr.make_config(base.pop("num_tokens"), base.pop("hidden"), base.pop("intermediate"), **base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_tokens=-1), L.MOE_ERR_INVALID_ARG),
+    (dict(hidden=0), L.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=3), L.MOE_ERR_INVALID_ARG),          # 256 % 3 != 0
+    (dict(topk_groups=9), L.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=8, topk_groups=1, topk=33), L.MOE_ERR_INVALID_ARG),
+    (dict(renormalize=True, routed_scaling=float("nan")), L.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=128, num_groups=8), L.MOE_ERR_UNSUPPORTED),
+    (dict(num_groups=128, topk_groups=4), L.MOE_ERR_UNSUPPORTED),
+    (dict(topk=9), L.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=320), L.MOE_ERR_UNSUPPORTED),
+    (dict(intermediate=96), L.MOE_ERR_UNSUPPORTED),
+    (dict(num_tokens=1 << 28), L.MOE_ERR_UNSUPPORTED),
+])
+def test_config_validation(kw, code):
+    cfg = _cfg(**kw)
+    n = ctypes.c_size_t(0)
+    assert gtr.lib().moe_workspace_bytes(ctypes.byref(cfg), L.ENTRY_LAYER, ctypes.byref(n)) == code
+
+
+def test_null_config_and_bad_entry():
+    n = ctypes.c_size_t(0)
+    assert gtr.lib().moe_workspace_bytes(None, 0, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
+    cfg = _cfg()
+    assert gtr.lib().moe_workspace_bytes(ctypes.byref(cfg), 9, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
+    assert gtr.lib().moe_workspace_bytes(ctypes.byref(cfg), 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_grow_with_tokens():
+    small = gtr.workspace_bytes(_cfg(num_tokens=32), L.ENTRY_LAYER)
+    big = gtr.workspace_bytes(_cfg(num_tokens=4096), L.ENTRY_LAYER)
+    assert 0 < small < big
+    for e in (L.ENTRY_ROUTE, L.ENTRY_PERMUTE, L.ENTRY_EXPERT_FFN):
+        assert 0 < gtr.workspace_bytes(_cfg(), e) <= gtr.workspace_bytes(_cfg(), L.ENTRY_LAYER)
+
+
+# Fake, never-dereferenced, 16-byte aligned "device" addresses: every call
+# below must fail validation on the host and enqueue nothing.
+A = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10004)
+
+
+def _layer(cfg, x=A, wr=A, wgu=A, wd=A, out=A, ws=A, nb=1 << 40):
+    return gtr.lib().moe_layer_forward(ctypes.byref(cfg), x, wr, None, wgu, wd, out, None, None,
+                                       ws, nb, None)
+
+
+def test_layer_rejects_null_and_misaligned_pointers():
+    cfg = _cfg()
+    assert _layer(cfg, x=None) == L.MOE_ERR_INVALID_ARG
+    assert _layer(cfg, wgu=None) == L.MOE_ERR_INVALID_ARG
+    assert _layer(cfg, out=None) == L.MOE_ERR_INVALID_ARG
+    assert _layer(cfg, x=MIS) == L.MOE_ERR_INVALID_ARG
+    assert _layer(cfg, wd=MIS) == L.MOE_ERR_INVALID_ARG
+
+
+def test_layer_rejects_small_or_missing_workspace():
+    cfg = _cfg()
+    need = gtr.workspace_bytes(cfg, L.ENTRY_LAYER)
+    assert _layer(cfg, nb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert _layer(cfg, ws=None, nb=need) == L.MOE_ERR_WORKSPACE
+    assert _layer(cfg, ws=MIS, nb=need) == L.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop():
+    cfg = _cfg(num_tokens=0)
+    need = gtr.workspace_bytes(cfg, L.ENTRY_LAYER)
+    assert _layer(cfg, nb=need) == L.MOE_OK
+    lib = gtr.lib()
+    assert lib.moe_combine(ctypes.byref(cfg), A, A, A, A, None) == L.MOE_OK
+
+
+def test_entry_points_reject_nulls():
+    cfg = _cfg()
+    lib = gtr.lib()
+    big = 1 << 40
+    assert lib.moe_route(ctypes.byref(cfg), None, A, None, A, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_replay(ctypes.byref(cfg), A, A, None, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(cfg), A, A, None, A, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), A, A, A, None, A, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(cfg), A, None, A, A, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(cfg), A, A, None, A, A, None, big, None) == L.MOE_ERR_WORKSPACE
+
+
+def test_no_device_reports_hip_error():
+    # In a container without a GPU a valid call must return MOE_ERR_HIP (the
+    # library never falls back to the CPU).  On a GPU machine this check is moot.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg = _cfg()
+    need = gtr.workspace_bytes(cfg, L.ENTRY_LAYER)
+    assert _layer(cfg, nb=need) == L.MOE_ERR_HIP
+
+
+def test_python_binding_requires_device_tensors():
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        gtr.route(x, torch.zeros(256, 256))

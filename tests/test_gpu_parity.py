@@ -1,0 +1,237 @@
+"""GPU parity of every entry point against the CPU oracle at oracle-sized
+shapes (the tiny workload: T=128, hidden 256, intermediate 128, 256 experts in
+8 groups of 32), plus ragged sizes, edge cases and determinism."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_top_routing_amd as gtr
+import oracle
+import synth
+from parity_util import assert_close, check_routing, say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    say("[tiny] generating inputs on", DEV)
+    d = synth.make_inputs("tiny", 0, device=DEV)
+    d["np"] = {k: to_np(d[k]) for k in ("x", "w_router", "w_gate_up", "w_down")}
+    return d
+
+
+def _rand_ids(T, k=8, E=256, seed=0, hot=None):
+    rng = np.random.default_rng(seed)
+    if hot is not None:
+        return np.tile(np.asarray(hot, np.int32), (T, 1))
+    return np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+# --------------------------------------------------------------------- route
+@pytest.mark.parametrize("G,KG,K,renorm,bias", [
+    (8, 4, 8, True, False),     # Beam's rule
+    (8, 4, 8, False, False),    # raw scores as weights
+    (8, 4, 8, True, True),      # selection bias on
+    (1, 1, 8, True, False),     # plain top-k
+    (4, 2, 6, True, False),
+    (64, 8, 8, True, False),    # groups of 4 experts
+    (16, 3, 5, False, False),
+    (8, 8, 1, True, False),     # argmax
+])
+def test_route(tiny, G, KG, K, renorm, bias):
+    say(f"[route] tiny G={G} kG={KG} k={K} renorm={renorm} bias={bias}")
+    sb = synth.make_sel_bias(tiny["workload"], 0, device=DEV) if bias else None
+    ids, w = gtr.route(tiny["x"], tiny["w_router"], sel_bias=sb, num_groups=G, topk_groups=KG,
+                       topk=K, renormalize=renorm)
+    torch.cuda.synchronize()
+    rr = oracle.route(tiny["np"]["x"], tiny["np"]["w_router"], n_groups=G, topk_groups=KG,
+                      topk=K, renormalize=renorm, sel_bias=None if sb is None else to_np(sb))
+    nf, nd = check_routing(to_np(ids), to_np(w), rr, n_groups=G, topk_groups=KG, topk=K)
+    say(f"  flagged={nf} differing={nd}")
+    # ids come out in (value desc, index asc) order
+    sel = rr.sel
+    g = np.take_along_axis(sel, to_np(ids).astype(np.int64), 1).astype(np.float64)
+    assert np.all(np.diff(g, axis=1) <= 1e-6)
+
+
+def test_route_replay(tiny):
+    say("[route_replay] tiny")
+    rr = oracle.route(tiny["np"]["x"], tiny["np"]["w_router"])
+    ids = torch.from_numpy(rr.ids.astype(np.int32)).to(DEV)
+    for renorm in (True, False):
+        w = gtr.route_replay(tiny["x"], tiny["w_router"], ids, renormalize=renorm)
+        ref, _ = oracle.route_replay(tiny["np"]["x"], tiny["np"]["w_router"], rr.ids,
+                                     renormalize=renorm)
+        np.testing.assert_allclose(to_np(w), ref, rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("T", [1, 3, 63, 65, 127])
+def test_route_ragged(tiny, T):
+    say(f"[route] tiny T={T}")
+    x = tiny["x"][:T].contiguous()
+    ids, w = gtr.route(x, tiny["w_router"])
+    rr = oracle.route(tiny["np"]["x"][:T], tiny["np"]["w_router"])
+    check_routing(to_np(ids), to_np(w), rr)
+
+
+def test_route_200_tokens():
+    # more tokens than one logits tile column, ragged against 64
+    say("[route] T=200 hidden 512")
+    w = synth.workload("tiny", T=200, H=512)
+    x = synth.make_x(w, 3, DEV)
+    wr = synth.make_router(w, 3, DEV)
+    ids, wt = gtr.route(x, wr)
+    check_routing(to_np(ids), to_np(wt), oracle.route(to_np(x), to_np(wr)))
+
+
+# ------------------------------------------------------------------- permute
+def _expected_perm(ids, E=256):
+    flat = ids.reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    idx = np.nonzero(valid)[0]
+    order = idx[np.argsort(flat[idx], kind="stable")]
+    dst = np.full(flat.size, -1, np.int64)
+    dst[order] = np.arange(order.size)
+    return counts, offsets, order, dst
+
+
+@pytest.mark.parametrize("T,hot", [(1, None), (3, None), (128, None), (513, None), (4097, None),
+                                   (2000, list(range(100, 108)))])
+def test_permute_exact(T, hot):
+    say(f"[permute] T={T} hot={hot is not None}")
+    ids = _rand_ids(T, seed=T, hot=hot)
+    c, o, ps, pd = gtr.permute(torch.from_numpy(ids).to(DEV))
+    rc, ro, rps, rpd = oracle.permute(ids, 256)
+    assert np.array_equal(to_np(c), rc)
+    assert np.array_equal(to_np(o), ro)
+    assert np.array_equal(to_np(ps), rps)
+    assert np.array_equal(to_np(pd), rpd)
+
+
+def test_permute_drops_out_of_range_ids():
+    say("[permute] out-of-range ids")
+    ids = _rand_ids(300, seed=5)
+    ids[3, 2] = -1
+    ids[77, 0] = 256
+    ids[299, 7] = 1 << 30
+    c, o, ps, pd = gtr.permute(torch.from_numpy(ids).to(DEV))
+    rc, ro, rorder, rdst = _expected_perm(ids)
+    n = int(ro[-1])
+    assert np.array_equal(to_np(c), rc) and np.array_equal(to_np(o), ro)
+    assert np.array_equal(to_np(ps)[:n], rorder)
+    assert np.array_equal(to_np(pd), rdst)
+
+
+# ----------------------------------------------------------------------- ffn
+def test_expert_ffn(tiny):
+    say("[expert_ffn] tiny")
+    npd = tiny["np"]
+    rr = oracle.route(npd["x"], npd["w_router"])
+    counts, offsets, psrc, pdst = oracle.permute(rr.ids, 256)
+    y = gtr.expert_ffn(tiny["x"], torch.from_numpy(psrc.astype(np.int32)).to(DEV),
+                       torch.from_numpy(offsets.astype(np.int32)).to(DEV),
+                       tiny["w_gate_up"], tiny["w_down"])
+    ref = oracle.expert_ffn(npd["x"], psrc, offsets, (npd["w_gate_up"], npd["w_down"]))
+    assert_close(to_np(y), ref, "y_perm")
+
+
+@pytest.mark.parametrize("hot_rows,T", [(1, 64), (17, 64), (40, 200), (130, 700), (300, 1024),
+                                        (1000, 2048)])
+def test_expert_ffn_ragged_tiles(tiny, hot_rows, T):
+    # one expert gets `hot_rows` rows, the rest spread thinly: m-tiles with
+    # ragged tails, experts with a single row, and every m-tile height the
+    # library picks from the mean rows per expert (T=64 -> 16 rows, 200/700 ->
+    # 32, 1024 -> 64, 2048 -> 128)
+    say(f"[expert_ffn] ragged hot_rows={hot_rows} T={T}")
+    npd = tiny["np"]
+    rng = np.random.default_rng(hot_rows)
+    ids = np.stack([rng.choice(np.arange(1, 256), 8, replace=False) for _ in range(T)])
+    ids[:hot_rows, 0] = 0
+    x = synth.make_x(synth.workload("tiny", T=T), 7, DEV)
+    xn = to_np(x)
+    counts, offsets, psrc, pdst = oracle.permute(ids, 256)
+    y = gtr.expert_ffn(x, torch.from_numpy(psrc.astype(np.int32)).to(DEV),
+                       torch.from_numpy(offsets.astype(np.int32)).to(DEV),
+                       tiny["w_gate_up"], tiny["w_down"])
+    ref = oracle.expert_ffn(xn, psrc, offsets, (npd["w_gate_up"], npd["w_down"]))
+    assert_close(to_np(y), ref, "y_perm")
+
+
+# ------------------------------------------------------------------- combine
+def test_combine(tiny):
+    say("[combine] tiny")
+    npd = tiny["np"]
+    rr = oracle.route(npd["x"], npd["w_router"])
+    counts, offsets, psrc, pdst = oracle.permute(rr.ids, 256)
+    y = oracle.expert_ffn(npd["x"], psrc, offsets, (npd["w_gate_up"], npd["w_down"]))
+    y_bf = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16)
+    w32 = rr.weights.astype(np.float32)
+    out = gtr.combine(y_bf.to(DEV), torch.from_numpy(pdst.astype(np.int32)).to(DEV),
+                      torch.from_numpy(w32).to(DEV), routed_scaling=2.5)
+    ref = oracle.combine(to_np(y_bf), pdst, w32.astype(np.float64), 2.5)
+    # only the final bf16 rounding separates the two
+    assert_close(to_np(out), ref, "combine", max_rel=8e-3, mean_rel=2e-3)
+
+
+# --------------------------------------------------------------------- layer
+@pytest.mark.parametrize("renorm,bias", [(True, False), (False, False), (True, True)])
+def test_layer(tiny, renorm, bias):
+    say(f"[layer] tiny renorm={renorm} bias={bias}")
+    npd = tiny["np"]
+    sb = synth.make_sel_bias(tiny["workload"], 0, device=DEV) if bias else None
+    out, ids, w = gtr.layer_forward(tiny["x"], tiny["w_router"], tiny["w_gate_up"],
+                                    tiny["w_down"], sel_bias=sb, renormalize=renorm,
+                                    return_routing=True)
+    ref = oracle.layer_forward(npd["x"], npd["w_router"], (npd["w_gate_up"], npd["w_down"]),
+                               renormalize=renorm, sel_bias=None if sb is None else to_np(sb))
+    nf, nd = check_routing(to_np(ids), to_np(w), ref["route"])
+    assert nd == 0, "tiny workload: no token should sit at a selection tie"
+    assert_close(to_np(out), ref["out"], "out")
+
+
+@pytest.mark.parametrize("T", [1, 5, 127, 129, 300])
+def test_layer_ragged_tokens(tiny, T):
+    say(f"[layer] tiny-shape T={T}")
+    npd = tiny["np"]
+    x = synth.make_x(synth.workload("tiny", T=T), 11, DEV)
+    out = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
+    ref = oracle.layer_forward(to_np(x), npd["w_router"], (npd["w_gate_up"], npd["w_down"]))
+    assert_close(to_np(out), ref["out"], "out")
+
+
+def test_layer_identical_experts_closed_form(tiny):
+    # every expert equal -> out = 2.5 * FFN_0(x) whatever the routing
+    say("[layer] identical experts")
+    wgu = tiny["w_gate_up"][:1].expand_as(tiny["w_gate_up"]).contiguous()
+    wd = tiny["w_down"][:1].expand_as(tiny["w_down"]).contiguous()
+    out = gtr.layer_forward(tiny["x"], tiny["w_router"], wgu, wd)
+    f0 = oracle.ffn_rows(tiny["np"]["x"], tiny["np"]["w_gate_up"][0], tiny["np"]["w_down"][0])
+    assert_close(to_np(out), 2.5 * f0, "out")
+
+
+def test_layer_deterministic_and_equivariant(tiny):
+    say("[layer] determinism / token permutation")
+    a = gtr.layer_forward(tiny["x"], tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
+    b = gtr.layer_forward(tiny["x"], tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
+    assert torch.equal(a, b)
+    P = torch.from_numpy(np.random.default_rng(1).permutation(128)).to(DEV)
+    c = gtr.layer_forward(tiny["x"][P].contiguous(), tiny["w_router"], tiny["w_gate_up"],
+                          tiny["w_down"])
+    assert torch.equal(a[P], c)
+
+
+def test_layer_on_side_stream(tiny):
+    say("[layer] non-default stream")
+    ref = gtr.layer_forward(tiny["x"], tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
+    s = torch.cuda.Stream(DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(s):
+        out = gtr.layer_forward(tiny["x"], tiny["w_router"], tiny["w_gate_up"], tiny["w_down"],
+                                workspace=gtr.Workspace())
+    torch.cuda.current_stream(DEV).wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
