@@ -67,3 +67,25 @@ def check_routing(ids_gpu, w_gpu, rr, *, n_groups=8, topk_groups=4, topk=8, w_rt
     m = ok | same
     np.testing.assert_allclose(w_gpu[m], w_ref[m], rtol=w_rtol, atol=1e-7)
     return int(flagged.sum()), int((flagged & ~same).sum())
+
+
+def layer_reference(ids_gpu, ref, x, experts, *, renormalize=True, scale=2.5):
+    """The oracle's layer output, except that tokens whose GPU expert set
+    differs from the oracle's (only allowed at a selection tie, see
+    check_routing) are evaluated by the oracle on the GPU's set, with weights
+    from the oracle's own scores."""
+    out = np.array(ref["out"], copy=True)
+    ids_gpu = np.asarray(ids_gpu).astype(np.int64)
+    rr = ref["route"]
+    get = experts if callable(experts) else (lambda e: (experts[0][e], experts[1][e]))
+    for t in range(ids_gpu.shape[0]):
+        S = ids_gpu[t]
+        if set(S.tolist()) == set(rr.ids[t].tolist()):
+            continue
+        s = rr.scores[t, S].astype(np.float64)
+        wt = s / s.sum() if renormalize else s
+        acc = np.zeros(out.shape[1])
+        for j, e in enumerate(S):
+            acc += wt[j] * oracle.ffn_rows(np.asarray(x)[t:t + 1], *get(int(e)))[0]
+        out[t] = scale * acc
+    return out

@@ -8,7 +8,7 @@ import torch
 import grouped_top_routing_amd as gtr
 import oracle
 import synth
-from parity_util import assert_close, check_routing, say, to_np
+from parity_util import assert_close, check_routing, layer_reference, say, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -189,18 +189,27 @@ def test_layer(tiny, renorm, bias):
     ref = oracle.layer_forward(npd["x"], npd["w_router"], (npd["w_gate_up"], npd["w_down"]),
                                renormalize=renorm, sel_bias=None if sb is None else to_np(sb))
     nf, nd = check_routing(to_np(ids), to_np(w), ref["route"])
-    assert nd == 0, "tiny workload: no token should sit at a selection tie"
-    assert_close(to_np(out), ref["out"], "out")
+    say(f"  flagged={nf} differing={nd}")
+    assert_close(to_np(out), layer_reference(to_np(ids), ref, npd["x"],
+                                             (npd["w_gate_up"], npd["w_down"]),
+                                             renormalize=renorm), "out")
 
 
 @pytest.mark.parametrize("T", [1, 5, 127, 129, 300])
 def test_layer_ragged_tokens(tiny, T):
     say(f"[layer] tiny-shape T={T}")
     npd = tiny["np"]
+    # seed 11 puts token 66 one ulp from a selection tie (margin 6e-8): the
+    # GPU may pick the other side; that token is then checked on the GPU's set
     x = synth.make_x(synth.workload("tiny", T=T), 11, DEV)
-    out = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
-    ref = oracle.layer_forward(to_np(x), npd["w_router"], (npd["w_gate_up"], npd["w_down"]))
-    assert_close(to_np(out), ref["out"], "out")
+    out, ids, w = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"],
+                                    return_routing=True)
+    xn = to_np(x)
+    ref = oracle.layer_forward(xn, npd["w_router"], (npd["w_gate_up"], npd["w_down"]))
+    nf, nd = check_routing(to_np(ids), to_np(w), ref["route"])
+    say(f"  flagged={nf} differing={nd}")
+    assert_close(to_np(out), layer_reference(to_np(ids), ref, xn,
+                                             (npd["w_gate_up"], npd["w_down"])), "out")
 
 
 def test_layer_identical_experts_closed_form(tiny):
