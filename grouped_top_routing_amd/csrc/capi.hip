@@ -4,7 +4,6 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
-#include <mutex>
 
 #include "../../include/beam_moe.h"
 #include "kernels.h"
@@ -102,30 +101,6 @@ int device_ready() {
   return hipGetDevice(&dev) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-// Persistent grid for the grouped GEMM: all CUs, 2 workgroups each (a
-// multiple of 8 so every XCD gets the same number of workgroups).
-int gemm_grid(int64_t max_items) {
-  static std::mutex mu;
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  int n = 0;
-  {
-    std::lock_guard<std::mutex> lk(mu);
-    if (dev < 64) n = cus[dev];
-    if (n == 0) {
-      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return -1;
-      if (dev < 64) cus[dev] = n;
-    }
-  }
-  int64_t grid = (int64_t)n * 2;
-  const int64_t cap = (max_items + 7) / 8 * 8;
-  if (cap < grid) grid = cap;
-  grid = (grid + 7) / 8 * 8;
-  return (int)(grid > 0 ? grid : 8);
-}
-
 // ---- internal steps (arguments already validated) ----
 int do_route(const moe_config_t* c, const uint16_t* x, const float* wr, const float* bias,
              int32_t* ids, float* w, void* scratch, hipStream_t s) {
@@ -152,22 +127,18 @@ int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
                const int32_t* plan, const uint16_t* wgu, uint16_t* h, hipStream_t s) {
   const int64_t max_tiles = max_tiles_for(c);
   const int H = c->hidden, I = c->intermediate;
-  const int grid = gemm_grid(max_tiles * (I / ffn_out_cols_per_item(true)));
-  if (grid < 0) return MOE_ERR_HIP;
   return hip_status(launch_grouped_gemm(mb_for(c), true, x, psrc, c->topk, wgu,
                                         (int64_t)2 * I * H, h, plan, (int)max_tiles, H, I, I,
-                                        grid, s));
+                                        max_tiles * (I / ffn_out_cols_per_item(true)), s));
 }
 
 int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint16_t* wd,
             uint16_t* y, hipStream_t s) {
   const int64_t max_tiles = max_tiles_for(c);
   const int H = c->hidden, I = c->intermediate;
-  const int grid = gemm_grid(max_tiles * (H / ffn_out_cols_per_item(false)));
-  if (grid < 0) return MOE_ERR_HIP;
   return hip_status(launch_grouped_gemm(mb_for(c), false, h, nullptr, c->topk, wd,
-                                        (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0, grid,
-                                        s));
+                                        (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0,
+                                        max_tiles * (H / ffn_out_cols_per_item(false)), s));
 }
 
 int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const int32_t* offsets,

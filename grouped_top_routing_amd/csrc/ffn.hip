@@ -10,52 +10,233 @@
 //             A_r = x[perm_src[r] / topk]   (row gather fused into the A load)
 //   down:     y[r, :] = bf16( h_r . Wd_e^T )
 //
-// Work decomposition.  A device-built plan (tile_plan_kernel) cuts each
-// expert's rows into m-tiles of at most 16*MB rows.  A work item is one
-// (m-tile, n-tile) pair; a persistent grid walks the items.  Items are dealt
-// so that a round of the grid gives consecutive items -- the n-tiles of one
-// m-tile, then the next m-tile of the same expert -- to workgroups of the same
-// XCD (workgroup b runs on XCD b % 8), so the gathered A rows and the expert's
-// weight rows are shared through that XCD's L2.
+// At every Beam batch size up to a few thousand tokens these GEMMs are bound
+// by streaming the touched experts' weights from HBM (a 4096-token chunk puts
+// ~128 rows on each expert: ~127 FLOP per weight byte, under the MI355X ridge
+// of ~315), so the kernel is built around keeping HBM busy:
 //
-// Inside an item: 4 waves; wave w owns NCB 16-column blocks of the weight
-// (for gate/up: NCB/2 gate blocks and the matching NCB/2 up blocks, so the
-// SwiGLU epilogue is wave-local).  Weights stream from HBM straight into
-// registers (each weight element is used by exactly one wave), one K-step
-// ahead.  The A tile (<= 16*MB rows x 64 k) is staged in LDS, double
-// buffered, XOR-swizzled by row so the 16 rows a fragment read touches hit
-// distinct banks.  MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
-//
-// Operand k-mapping: within a K-step of 64, lane (r = lane%16, g = lane/16)
-// holds k in [16g, 16g+16) of its A row and of its weight row; sub-step s
-// (0, 1) feeds the MFMA the 8 values [16g + 8s, 16g + 8s + 8).  Both operands
-// use the same mapping, so each MFMA sums matching k.
+// * Weights and activations go global -> LDS with gfx950's direct loads
+//   (global_load_lds_dwordx4: 64 lanes x 16 B into 1 KB of LDS, no VGPRs),
+//   through an S-stage ring.  S-1 stages of 32 k are always in flight; each
+//   wave waits on its own vmcnt and one s_barrier per stage publishes the
+//   stage to the other waves.
+// * One 1 KB "fragment" is exactly one MFMA operand (16 rows x 32 k, bf16):
+//   lane l fetches row l%16, k chunk (l/16)*8, and later reads the same 16
+//   bytes back with a conflict-free ds_read_b128 at lane*16.  Every operand
+//   is loaded and read in the v_mfma_f32_16x16x32_bf16 lane order, so A and B
+//   lanes always carry matching k.
+// * A work item is one (m-tile, n-tile) pair.  A device-built plan cuts each
+//   expert's rows into balanced m-tiles of at most 16*MB rows, so at Beam's
+//   prefill size an expert's rows fit one m-tile and its weights are fetched
+//   once.  Wave w owns NCBW 16-column weight blocks (for gate/up: NCBW/2 gate
+//   blocks and the matching up blocks, so the SwiGLU epilogue is wave-local).
+// * A persistent grid walks the items.  Workgroup b runs on XCD b % 8; items
+//   are dealt so that the n-tiles of one m-tile land on one XCD in the same
+//   round, sharing the gathered A rows through that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace beam {
 
-constexpr int kBK = 64;  // K per pipeline step
+constexpr int kBKS = 32;     // k per pipeline stage (one MFMA k)
+constexpr int kNW = 4;       // waves per workgroup
+constexpr int kFrag = 1024;  // bytes of one 16 x 32 bf16 MFMA operand
 
-// LDS byte offset of 16-byte chunk c (0..7) of A-tile row `row`.
-__device__ __forceinline__ int a_lds_off(int row, int c) {
-  return row * (kBK * 2) + ((c ^ (row & 7)) << 4);
+// s_waitcnt immediate (GFX9 encoding) that waits until at most n vector
+// memory operations of this wave are outstanding; other counters untouched.
+__host__ __device__ constexpr int vm_wait_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-template <int MB, int NCB, bool SWIGLU>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
+}
+
+// Compiler-level fence: no memory access moves across it (emits nothing).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding direct load).
+__device__ __forceinline__ void stage_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+template <int AHEAD, int L>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  // wait until only `ahead` later stages (L loads each) remain in flight
+  if constexpr (AHEAD == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= AHEAD) wait_vm<AHEAD * L>();
+    else wait_stage<AHEAD - 1, L>(ahead);
+  }
+}
+
+// One direct global -> LDS load: lane l's 16 bytes at `g` land at LDS byte
+// address lds_addr + 16*l (lds_addr must be wave-uniform; it goes in M0).
+// Issued from inline asm so the compiler's own wait-count pass does not see
+// it: the pass would otherwise put a vmcnt(0) -- a full drain of the ring --
+// before every later LDS read.  Completion is tracked by hand with
+// wait_vm<>() (vector memory operations of a wave complete in order).  M0 is
+// saved and restored, and s_nop covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_addr)
+      : "memory");
+}
+
+// Everything one work item needs, resolved once per item.
+struct ItemArgs {
+  const uint16_t* A;
+  const int32_t* gather;
+  int topk;
+  const uint16_t* W;       // this expert's weight rows
+  uint16_t* C;
+  int K, n_out, up_row0;
+  int row0, nrows, ntile;
+};
+
+// One (m-tile, n-tile) item with exactly NRB live 16-row blocks.  MB sizes the
+// LDS ring; fragments of blocks NRB..MB-1 are not loaded.
+template <int NRB, int MB, int NCBW, int S, bool SWIGLU>
+__device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int wave, int lane) {
+  constexpr int D = S - 1;                      // stages in flight ahead of compute
+  constexpr int AOFF = kNW * NCBW * kFrag;      // slot = B fragments, then A fragments
+  constexpr int SLOT = AOFF + MB * kFrag;
+  constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
+  constexpr int WCOLS = kNW * HALF * 16;
+  // A fragments of this wave: blocks wave, wave+4, ... below NRB
+  constexpr int AMAX = (NRB + kNW - 1) / kNW;
+  const int r = lane & 15, g = lane >> 4;
+  const int nk = a.K / kBKS;
+  // Waves own different numbers of A fragments when NRB % 4 != 0, so each
+  // wave's loads per stage (and thus its vmcnt thresholds) are its own:
+  // na in {AMAX - 1, AMAX}.  Both values are handled by separate waits.
+  const int na = (NRB - wave + kNW - 1) / kNW;
+
+  const uint16_t* asrc[AMAX > 0 ? AMAX : 1];
+#pragma unroll
+  for (int j = 0; j < AMAX; ++j) {
+    int row = (wave + kNW * j) * 16 + r;
+    row = row < a.nrows ? row : a.nrows - 1;  // rows past the tile repeat its last row
+    const int src = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
+    asrc[j] = a.A + (size_t)src * a.K + 8 * g;
+  }
+  const uint16_t* bsrc[NCBW];
+#pragma unroll
+  for (int cb = 0; cb < NCBW; ++cb) {
+    int wrow;
+    if (SWIGLU) {
+      const int j = cb % HALF;
+      wrow = a.ntile * WCOLS + wave * HALF * 16 + j * 16 + r + (cb >= HALF ? a.up_row0 : 0);
+    } else {
+      wrow = a.ntile * WCOLS + wave * NCBW * 16 + cb * 16 + r;
+    }
+    bsrc[cb] = a.W + (size_t)wrow * a.K + 8 * g;
+  }
+  // LDS byte offset of the ring (addrspace cast, not the flat address)
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
+  const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds0 + wave * NCBW * kFrag);
+  const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds0 + AOFF + wave * kFrag);
+
+  auto issue = [&](int st) {
+    const uint32_t so = (uint32_t)((st % S) * SLOT);
+    const int k0 = st * kBKS;
+#pragma unroll
+    for (int cb = 0; cb < NCBW; ++cb) lds_dma16(bsrc[cb] + k0, b_base + so + cb * kFrag);
+#pragma unroll
+    for (int j = 0; j < AMAX; ++j)
+      if (j < na) lds_dma16(asrc[j] + k0, a_base + so + kNW * j * kFrag);
+  };
+
+  f32x4_t acc[NRB][NCBW];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < D; ++st)
+    if (st < nk) issue(st);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(D - 1, nk - 1 - kt);
+    if (na == AMAX) wait_stage<D - 1, NCBW + AMAX>(ahead);
+    else wait_stage<D - 1, NCBW + AMAX - 1>(ahead);
+    stage_barrier();  // stage kt visible to all waves; slot (kt-1)%S is free
+    if (kt + D < nk) issue(kt + D);
+    const uint8_t* sl = lds + (kt % S) * SLOT;
+    uint4 bf[NCBW], af[NRB];
+#pragma unroll
+    for (int cb = 0; cb < NCBW; ++cb)
+      bf[cb] = *reinterpret_cast<const uint4*>(sl + (wave * NCBW + cb) * kFrag + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+      af[i] = *reinterpret_cast<const uint4*>(sl + AOFF + i * kFrag + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int cb = 0; cb < NCBW; ++cb)
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bf[cb]),
+                                                             acc[i][cb], 0, 0, 0);
+  }
+  stage_barrier();  // every wave is done with the ring before the next item refills it
+
+  // epilogue: lane holds rows 4g..4g+3 of column r of each 16x16 block
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+      const int col = a.ntile * WCOLS + wave * HALF * 16 + j * 16 + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i * 16 + 4 * g + v;
+        float o;
+        if (SWIGLU) {
+          const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
+          o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+        } else {
+          o = acc[i][j][v];
+        }
+        if (row < a.nrows) a.C[(size_t)(a.row0 + row) * a.n_out + col] = (uint16_t)f32_to_bf16(o);
+      }
+    }
+  }
+}
+
+template <int N, int MB, int NCBW, int S, bool SWIGLU>
+__device__ __forceinline__ void gemm_item_dispatch(int nrb, const ItemArgs& a, uint8_t* lds,
+                                                   int wave, int lane) {
+  if constexpr (N > MB) {
+    return;
+  } else {
+    if (nrb == N) gemm_item<N, MB, NCBW, S, SWIGLU>(a, lds, wave, lane);
+    else gemm_item_dispatch<N + 1, MB, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
+  }
+}
+
+template <int MB, int NCBW, int S, bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
     const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0) {
-  constexpr int ROWS = 16 * MB;
-  constexpr int HALF = SWIGLU ? NCB / 2 : NCB;    // output column blocks per wave
-  constexpr int WCOLS = 4 * HALF * 16;            // output columns per item
-  constexpr int LOADERS = ROWS * 8;               // threads that stage A (16 B each)
-  constexpr int APASS = (LOADERS + 255) / 256;    // staging passes per thread
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][ROWS * kBK * 2];
+  constexpr int SLOT = (kNW * NCBW + MB) * kFrag;
+  constexpr int WCOLS = kNW * (SWIGLU ? NCBW / 2 : NCBW) * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * SLOT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntiles = plan[0];
   const int* plan_expert = plan + 4;
   const int* plan_row0 = plan_expert + max_tiles;
@@ -64,133 +245,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
   const int total = ntiles * nt_n;
   const int grid = gridDim.x, per_xcd = grid / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int nk = K / kBK;
 
   for (int round = 0;; round += grid) {
     const int q = round + xcd * per_xcd + slot;
     if (q >= total) break;
-    const int tile = q / nt_n, ntile = q - tile * nt_n;
-    const int e = plan_expert[tile], row0 = plan_row0[tile], nrows = plan_rows[tile];
-    const int nrb = (nrows + 15) >> 4;
-
-    // --- A staging addresses (row gather happens here) ---
-    const uint16_t* a_src[APASS];
-    int a_off[APASS];
-    bool a_ok[APASS];
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      const int li = p * 256 + tid;
-      const int row = li >> 3, c = li & 7;
-      a_ok[p] = li < LOADERS && row < nrows;
-      a_off[p] = a_lds_off(row < ROWS ? row : 0, c);
-      int src_row = 0;
-      if (a_ok[p]) src_row = gather ? gather[row0 + row] / topk : row0 + row;
-      a_src[p] = A + (size_t)src_row * K + c * 8;
-    }
-
-    // --- weight row pointers of this wave ---
-    const uint16_t* wp[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      int wrow;
-      if (SWIGLU) {
-        const int j = cb % HALF;
-        wrow = ntile * WCOLS + wave * HALF * 16 + j * 16 + r + (cb >= HALF ? up_row0 : 0);
-      } else {
-        wrow = ntile * WCOLS + wave * NCB * 16 + cb * 16 + r;
-      }
-      wp[cb] = W + (size_t)e * w_expert_stride + (size_t)wrow * K + 16 * g;
-    }
-
-    f32x4_t acc[MB][NCB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // --- prologue: stage K-step 0 ---
-    uint4 areg[APASS];
-    uint4 bcur[NCB][2], bnxt[NCB][2];
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) areg[p] = a_ok[p] ? ld16(a_src[p]) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      bcur[cb][0] = ld16(wp[cb]);
-      bcur[cb][1] = ld16(wp[cb] + 8);
-    }
-    __syncthreads();  // previous item's last LDS reads are done
-#pragma unroll
-    for (int p = 0; p < APASS; ++p)
-      if (p * 256 + tid < LOADERS) *reinterpret_cast<uint4*>(&lds_a[0][a_off[p]]) = areg[p];
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int k1 = (kt + 1) * kBK;
-#pragma unroll
-        for (int p = 0; p < APASS; ++p)
-          areg[p] = a_ok[p] ? ld16(a_src[p] + k1) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          bnxt[cb][0] = ld16(wp[cb] + k1);
-          bnxt[cb][1] = ld16(wp[cb] + k1 + 8);
-        }
-      }
-      const uint8_t* la = lds_a[cur];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          if (i < nrb) {
-            const uint4 av = *reinterpret_cast<const uint4*>(la + a_lds_off(i * 16 + r, 2 * g + s));
-            const bf16x8_t a8 = as_bf16x8(av);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-              acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(bcur[cb][s]),
-                                                                   acc[i][cb], 0, 0, 0);
-          }
-        }
-      }
-      if (more) {
-#pragma unroll
-        for (int p = 0; p < APASS; ++p)
-          if (p * 256 + tid < LOADERS)
-            *reinterpret_cast<uint4*>(&lds_a[cur ^ 1][a_off[p]]) = areg[p];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          bcur[cb][0] = bnxt[cb][0];
-          bcur[cb][1] = bnxt[cb][1];
-        }
-      }
-      __syncthreads();
-    }
-
-    // --- epilogue: lane holds rows 4g..4g+3 of column r of each 16x16 block ---
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      if (i < nrb) {
-#pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-          const int col = ntile * WCOLS + wave * HALF * 16 + j * 16 + r;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = i * 16 + 4 * g + v;
-            if (row < nrows) {
-              float o;
-              if (SWIGLU) {
-                const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
-                o = gt / (1.0f + expf(-gt)) * up;
-              } else {
-                o = acc[i][j][v];
-              }
-              C[(size_t)(row0 + row) * n_out + col] = (uint16_t)f32_to_bf16(o);
-            }
-          }
-        }
-      }
-    }
+    const int tile = q / nt_n;
+    const int e = plan_expert[tile];
+    ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0,
+               plan_row0[tile], plan_rows[tile], q - tile * nt_n};
+    const int nrb = (a.nrows + 15) >> 4;
+    gemm_item_dispatch<1, MB, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
   }
 }
 
@@ -231,26 +295,50 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* __restric
   if (e == 255) plan[0] = min(sc[255], max_tiles);
 }
 
-template <int MB, int NCB, bool SWIGLU>
-static hipError_t launch_gemm_t(const uint16_t* A, const int32_t* gather, int topk,
+// ---------------------------------------------------------------------------
+// Launch configurations: (MB, NCBW, S).  LDS per workgroup = S * (16 + MB) KB.
+constexpr int kNCBW = 4;
+
+template <int MB, int S, bool SWIGLU>
+static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int topk,
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                                int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<MB, NCB, SWIGLU>), dim3(grid), dim3(256), 0, stream, A,
-                     gather, topk, W, wstride, C, plan, max_tiles, K, n_out, up_row0);
+                                int64_t max_items, hipStream_t stream) {
+  auto kern = stream_gemm_kernel<MB, kNCBW, S, SWIGLU>;
+  static int per_cu = 0;  // resident workgroups per CU, fixed per build
+  static int cus = 0;
+  if (per_cu == 0) {
+    int dev = 0, n = 0, occ = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0);
+    if (err != hipSuccess) return err;
+    cus = n;
+    per_cu = occ > 0 ? occ : 1;
+  }
+  int64_t grid = (int64_t)cus * per_cu;
+  const int64_t cap = (max_items + 7) / 8 * 8;
+  if (cap < grid) grid = cap;
+  grid = (grid + 7) / 8 * 8;
+  if (grid < 8) grid = 8;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, A, gather, topk, W, wstride,
+                     C, plan, max_tiles, K, n_out, up_row0);
   return hipGetLastError();
 }
 
 int ffn_rows_per_tile(int mb) { return 16 * mb; }
 
-// Picks the m-tile height from the mean rows per expert.
+// m-tile height from the mean rows per expert: 64 rows while experts hold a
+// few dozen rows (decode, mid batches), 192 once they hold ~100 or more, so
+// an expert of a 4096-token chunk (95..165 rows) is a single m-tile.
 int ffn_choose_mb(int64_t rows, int E) {
   const int64_t mean = rows / (E > 0 ? E : 1);
-  if (mean <= 8) return 1;
-  if (mean <= 24) return 2;
-  if (mean <= 48) return 4;
-  return 8;
+  if (mean <= 40) return 4;
+  if (mean <= 80) return 8;
+  return 12;
 }
+
+int ffn_out_cols_per_item(bool swiglu) { return kNW * (swiglu ? kNCBW / 2 : kNCBW) * 16; }
 
 hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* plan, int max_tiles,
                             hipStream_t stream) {
@@ -262,25 +350,21 @@ hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* pl
 hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                               int grid, hipStream_t stream) {
-  constexpr int NCB = 4;
-#define BEAM_GEMM_CASE(MBV)                                                                     \
+                               int64_t max_items, hipStream_t stream) {
+#define BEAM_STREAM_CASE(MBV, SV)                                                               \
   case MBV:                                                                                     \
-    return swiglu ? launch_gemm_t<MBV, NCB, true>(A, gather, topk, W, wstride, C, plan,         \
-                                                  max_tiles, K, n_out, up_row0, grid, stream)   \
-                  : launch_gemm_t<MBV, NCB, false>(A, gather, topk, W, wstride, C, plan,        \
-                                                   max_tiles, K, n_out, up_row0, grid, stream);
+    return swiglu ? launch_stream<MBV, SV, true>(A, gather, topk, W, wstride, C, plan,          \
+                                                 max_tiles, K, n_out, up_row0, max_items, stream) \
+                  : launch_stream<MBV, SV, false>(A, gather, topk, W, wstride, C, plan,         \
+                                                  max_tiles, K, n_out, up_row0, max_items, stream);
   switch (mb) {
-    BEAM_GEMM_CASE(1)
-    BEAM_GEMM_CASE(2)
-    BEAM_GEMM_CASE(4)
-    BEAM_GEMM_CASE(8)
+    BEAM_STREAM_CASE(4, 4)
+    BEAM_STREAM_CASE(8, 5)
+    BEAM_STREAM_CASE(12, 5)
     default:
       return hipErrorInvalidValue;
   }
-#undef BEAM_GEMM_CASE
+#undef BEAM_STREAM_CASE
 }
-
-int ffn_out_cols_per_item(bool swiglu) { return swiglu ? 4 * 2 * 16 : 4 * 4 * 16; }
 
 }  // namespace beam
