@@ -69,7 +69,8 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
     dev = wts["dev"]
     w = synth.workload(name)
     x = synth.make_x(w, args.seed, dev, w_router=wts["w_router"])
-    wr, wgu, wd = wts["w_router"], wts["w_gate_up"], wts["w_down"]
+    wr, wgu, wd = wts["w_router"], wts["p_gate_up"], wts["p_down"]
+    lay = gtr.LAYOUT_PACKED
     ws = gtr.Workspace()
 
     def step(ev=None):
@@ -81,10 +82,10 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
         c, o, ps, pd = gtr.permute(ids, workspace=ws)
         if ev is not None:
             ev[2].record()
-        h = gtr.expert_gate_up(x, ps, o, wgu, workspace=ws)
+        h = gtr.expert_gate_up(x, ps, o, wgu, weight_layout=lay, workspace=ws)
         if ev is not None:
             ev[3].record()
-        y = gtr.expert_down(h, o, wd, workspace=ws)
+        y = gtr.expert_down(h, o, wd, weight_layout=lay, workspace=ws)
         if ev is not None:
             ev[4].record()
         out = gtr.combine(y, pd, tw)
@@ -105,17 +106,21 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
     names = ["route", "permute", "gate_up", "down", "combine"]
     stage = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
              for j, n in enumerate(names)}
-    # the single-call entry point, for reference
-    for _ in range(2):
-        gtr.layer_forward(x, wr, wgu, wd, workspace=ws)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(steps):
-        gtr.layer_forward(x, wr, wgu, wd, workspace=ws)
-    torch.cuda.synchronize()
-    layer_ms = (time.perf_counter() - t1) * 1e3 / steps
+    # the single-call entry point, for reference, in both weight layouts
+    def time_layer(a, b, layout):
+        for _ in range(2):
+            gtr.layer_forward(x, wr, a, b, weight_layout=layout, workspace=ws)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            gtr.layer_forward(x, wr, a, b, weight_layout=layout, workspace=ws)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t1) * 1e3 / steps
+    layer_ms = time_layer(wgu, wd, lay)
+    rowmajor_ms = time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR)
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
-            "layer_forward_ms": layer_ms, "counts": counts.cpu().numpy(), "ids": ids}
+            "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
+            "counts": counts.cpu().numpy(), "ids": ids}
 
 
 def cpu_baseline(w, x, wts, n_experts, torch):
@@ -177,6 +182,8 @@ def main():
           f"bf16) on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
     wts = {"dev": dev, "w_router": synth.make_router(beam, args.seed, dev)}
     wts["w_gate_up"], wts["w_down"] = synth.make_experts(beam, args.seed, dev)
+    # the library's fragment-packed weight layout, written once at load time
+    wts["p_gate_up"], wts["p_down"] = gtr.pack_weights(wts["w_gate_up"], wts["w_down"])
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}",
@@ -211,6 +218,8 @@ def main():
                   "bf16_mfma_frac": round(mfma_frac, 4), "algorithmic_bytes": alg["layer_bytes"],
                   "expert_flops": alg["expert_flops"], "touched_experts": alg["touched"],
                   "layer_forward_ms": round(r["layer_forward_ms"], 4),
+                  "row_major_weights_layer_ms": round(r["row_major_layer_ms"], 4),
+                  "weight_layout": "packed (moe_pack_weights, once at load)",
                   "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
                   "histogram": {"max": int(c.max()), "min": int(c.min()),
                                 "lt10": int((c < 10).sum()), "empty": int((c == 0).sum())}},

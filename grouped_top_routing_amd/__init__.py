@@ -11,7 +11,7 @@ include/beam_moe.h); this package only marshals torch tensors into it.
 """
 from ._lib import (  # noqa: F401
     ENTRY_EXPERT_FFN, ENTRY_EXPERT_STAGE, ENTRY_LAYER, ENTRY_PERMUTE, ENTRY_ROUTE, EXPORTS,
-    LIB_PATH, MoeConfig, MoeError, Workspace, combine, expert_down, expert_ffn, expert_gate_up,
-    layer_forward, lib, make_config, permute, route, route_replay, status_string,
-    workspace_bytes,
+    LAYOUT_PACKED, LAYOUT_ROW_MAJOR, LIB_PATH, MoeConfig, MoeError, Workspace, combine,
+    expert_down, expert_ffn, expert_gate_up, layer_forward, lib, make_config, pack_weights,
+    permute, route, route_replay, status_string, workspace_bytes,
 )

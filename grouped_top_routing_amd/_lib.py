@@ -27,10 +27,13 @@ ENTRY_EXPERT_FFN = 2
 ENTRY_LAYER = 3
 ENTRY_EXPERT_STAGE = 4
 
+LAYOUT_ROW_MAJOR = 0
+LAYOUT_PACKED = 1
+
 #: Every symbol include/beam_moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_replay", "moe_permute",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_layer_forward", "moe_status_string")
+           "moe_layer_forward", "moe_pack_weights", "moe_status_string")
 
 
 class MoeConfig(ctypes.Structure):
@@ -44,6 +47,7 @@ class MoeConfig(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("renormalize", ctypes.c_int32),
         ("routed_scaling", ctypes.c_float),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -74,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gate_up.argtypes = [CP, P, P, P, P, P, P, Z, P]
         L.moe_expert_down.argtypes = [CP, P, P, P, P, P, Z, P]
         L.moe_combine.argtypes = [CP, P, P, P, P, P]
+        L.moe_pack_weights.argtypes = [CP, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
         L.moe_status_string.argtypes = [I]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -89,10 +94,11 @@ def status_string(code: int) -> str:
 
 
 def make_config(num_tokens, hidden, intermediate, *, num_experts=256, num_groups=8,
-                topk_groups=4, topk=8, renormalize=True, routed_scaling=2.5) -> MoeConfig:
+                topk_groups=4, topk=8, renormalize=True, routed_scaling=2.5,
+                weight_layout=LAYOUT_ROW_MAJOR) -> MoeConfig:
     return MoeConfig(int(num_tokens), int(hidden), int(intermediate), int(num_experts),
                      int(num_groups), int(topk_groups), int(topk), int(bool(renormalize)),
-                     float(routed_scaling))
+                     float(routed_scaling), int(weight_layout))
 
 
 def workspace_bytes(cfg: MoeConfig, entry: int) -> int:
@@ -211,7 +217,8 @@ def permute(topk_ids, *, num_experts=256, workspace=None):
     return counts, offsets, psrc, pdst
 
 
-def expert_ffn(x, perm_src, offsets, w_gate_up, w_down, *, topk=8, workspace=None):
+def expert_ffn(x, perm_src, offsets, w_gate_up, w_down, *, topk=8, weight_layout=LAYOUT_ROW_MAJOR,
+               workspace=None):
     """Expert SwiGLU MLPs over the permuted rows: y_perm bf16 [T*k, H]."""
     T, H = x.shape
     E, I2, _ = w_gate_up.shape
@@ -221,7 +228,8 @@ def expert_ffn(x, perm_src, offsets, w_gate_up, w_down, *, topk=8, workspace=Non
     _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
     _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
     _check(w_down, "w_down", torch.bfloat16, (E, H, I), x.device)
-    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=weight_layout)
     y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=x.device)
     nb = workspace_bytes(cfg, ENTRY_EXPERT_FFN)
     ws = _ws(workspace, x.device).get(nb, x.device)
@@ -231,7 +239,8 @@ def expert_ffn(x, perm_src, offsets, w_gate_up, w_down, *, topk=8, workspace=Non
     return y
 
 
-def expert_gate_up(x, perm_src, offsets, w_gate_up, *, topk=8, workspace=None):
+def expert_gate_up(x, perm_src, offsets, w_gate_up, *, topk=8, weight_layout=LAYOUT_ROW_MAJOR,
+                   workspace=None):
     """First expert GEMM with the fused SwiGLU: h bf16 [T*k, I]."""
     T, H = x.shape
     E, I2, _ = w_gate_up.shape
@@ -240,7 +249,8 @@ def expert_gate_up(x, perm_src, offsets, w_gate_up, *, topk=8, workspace=None):
     _check(perm_src, "perm_src", torch.int32, (T * topk,), x.device)
     _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
     _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
-    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=weight_layout)
     h = torch.empty(T * topk, I, dtype=torch.bfloat16, device=x.device)
     nb = workspace_bytes(cfg, ENTRY_EXPERT_STAGE)
     ws = _ws(workspace, x.device).get(nb, x.device)
@@ -250,7 +260,7 @@ def expert_gate_up(x, perm_src, offsets, w_gate_up, *, topk=8, workspace=None):
     return h
 
 
-def expert_down(h, offsets, w_down, *, topk=8, workspace=None):
+def expert_down(h, offsets, w_down, *, topk=8, weight_layout=LAYOUT_ROW_MAJOR, workspace=None):
     """Second expert GEMM: y_perm bf16 [T*k, H]."""
     R, I = h.shape
     E, H, _ = w_down.shape
@@ -258,7 +268,8 @@ def expert_down(h, offsets, w_down, *, topk=8, workspace=None):
     _check(h, "h", torch.bfloat16, (T * topk, I))
     _check(offsets, "offsets", torch.int32, (E + 1,), h.device)
     _check(w_down, "w_down", torch.bfloat16, (E, H, I), h.device)
-    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=weight_layout)
     y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=h.device)
     nb = workspace_bytes(cfg, ENTRY_EXPERT_STAGE)
     ws = _ws(workspace, h.device).get(nb, h.device)
@@ -284,8 +295,8 @@ def combine(y_perm, perm_dst, topk_w, *, routed_scaling=2.5):
 
 
 def layer_forward(x, w_router, w_gate_up, w_down, *, sel_bias=None, num_groups=8, topk_groups=4,
-                  topk=8, renormalize=True, routed_scaling=2.5, return_routing=False,
-                  out=None, workspace=None):
+                  topk=8, renormalize=True, routed_scaling=2.5, weight_layout=LAYOUT_ROW_MAJOR,
+                  return_routing=False, out=None, workspace=None):
     """The whole MoE block.  Returns out bf16 [T, H] (and (ids, w) if asked)."""
     T, H = x.shape
     E, I2, _ = w_gate_up.shape
@@ -297,7 +308,8 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, sel_bias=None, num_groups=8
     if sel_bias is not None:
         _check(sel_bias, "sel_bias", torch.float32, (E,), x.device)
     cfg = make_config(T, H, I, num_experts=E, num_groups=num_groups, topk_groups=topk_groups,
-                      topk=topk, renormalize=renormalize, routed_scaling=routed_scaling)
+                      topk=topk, renormalize=renormalize, routed_scaling=routed_scaling,
+                      weight_layout=weight_layout)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     else:
@@ -313,3 +325,27 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, sel_bias=None, num_groups=8
                                   _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(ids), _ptr(w),
                                   _ptr(ws), nb, _stream(x.device)))
     return (out, ids, w) if return_routing else out
+
+
+def pack_weights(w_gate_up=None, w_down=None):
+    """Fragment-packed copies of the expert weights (MOE_LAYOUT_PACKED), same
+    shapes and dtype as the inputs.  Either argument may be None."""
+    ref = w_gate_up if w_gate_up is not None else w_down
+    if ref is None:
+        raise ValueError("pack_weights: nothing to pack")
+    if w_gate_up is not None:
+        E, I2, H = w_gate_up.shape
+        I = I2 // 2
+        _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H))
+    if w_down is not None:
+        E, H, I = w_down.shape
+        _check(w_down, "w_down", torch.bfloat16, (E, H, I), ref.device)
+        if w_gate_up is not None and tuple(w_gate_up.shape) != (E, 2 * I, H):
+            raise ValueError("w_gate_up and w_down shapes disagree")
+    cfg = make_config(0, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=1)
+    pgu = torch.empty_like(w_gate_up) if w_gate_up is not None else None
+    pd = torch.empty_like(w_down) if w_down is not None else None
+    _call("moe_pack_weights", lib().moe_pack_weights(ctypes.byref(cfg), _ptr(w_gate_up),
+                                                     _ptr(w_down), _ptr(pgu), _ptr(pd),
+                                                     _stream(ref.device)))
+    return pgu, pd

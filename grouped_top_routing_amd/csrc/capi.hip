@@ -27,6 +27,8 @@ int validate(const moe_config_t* c) {
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->routed_scaling)) return MOE_ERR_INVALID_ARG;
   if (c->num_experts % c->num_groups != 0) return MOE_ERR_INVALID_ARG;
+  if (c->weight_layout != MOE_LAYOUT_ROW_MAJOR && c->weight_layout != MOE_LAYOUT_PACKED)
+    return MOE_ERR_INVALID_ARG;
   if (c->topk_groups > c->num_groups) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c->topk > (int64_t)c->topk_groups * (c->num_experts / c->num_groups))
     return MOE_ERR_INVALID_ARG;
@@ -129,6 +131,7 @@ int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
   const int H = c->hidden, I = c->intermediate;
   return hip_status(launch_grouped_gemm(mb_for(c), true, x, psrc, c->topk, wgu,
                                         (int64_t)2 * I * H, h, plan, (int)max_tiles, H, I, I,
+                                        c->weight_layout,
                                         max_tiles * (I / ffn_out_cols_per_item(true)), s));
 }
 
@@ -138,6 +141,7 @@ int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const
   const int H = c->hidden, I = c->intermediate;
   return hip_status(launch_grouped_gemm(mb_for(c), false, h, nullptr, c->topk, wd,
                                         (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0,
+                                        c->weight_layout,
                                         max_tiles * (H / ffn_out_cols_per_item(false)), s));
 }
 
@@ -282,6 +286,37 @@ int moe_expert_down(const moe_config_t* cfg, const uint16_t* h, const int32_t* o
   int32_t* plan = static_cast<int32_t*>(workspace);
   if ((st = do_plan(cfg, offsets, plan, s))) return st;
   return do_down(cfg, h, plan, w_down, y_perm, s);
+}
+
+int moe_pack_weights(const moe_config_t* cfg, const uint16_t* w_gate_up, const uint16_t* w_down,
+                     uint16_t* packed_gate_up, uint16_t* packed_down, void* stream) {
+  moe_config_t c = cfg ? *cfg : moe_config_t{};
+  c.num_tokens = 0;
+  int st = validate(cfg ? &c : nullptr);
+  if (st) return st;
+  if ((w_gate_up == nullptr) != (packed_gate_up == nullptr) ||
+      (w_down == nullptr) != (packed_down == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if ((w_gate_up && (!aligned16(w_gate_up) || !aligned16(packed_gate_up))) ||
+      (w_down && (!aligned16(w_down) || !aligned16(packed_down))))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t E = c.num_experts, H = c.hidden, I = c.intermediate;
+  auto overlap = [](const void* a, const void* b, int64_t n) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + n && y < x + n;
+  };
+  if (w_gate_up && overlap(w_gate_up, packed_gate_up, E * 2 * I * H * 2)) return MOE_ERR_INVALID_ARG;
+  if (w_down && overlap(w_down, packed_down, E * H * I * 2)) return MOE_ERR_INVALID_ARG;
+  if (!w_gate_up && !w_down) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w_gate_up &&
+      (st = hip_status(launch_pack_weights(w_gate_up, packed_gate_up, (int)E, (int)(2 * I), (int)H, s))))
+    return st;
+  if (w_down && (st = hip_status(launch_pack_weights(w_down, packed_down, (int)E, (int)H, (int)I, s))))
+    return st;
+  return MOE_OK;
 }
 
 int moe_combine(const moe_config_t* cfg, const uint16_t* y_perm, const int32_t* perm_dst,

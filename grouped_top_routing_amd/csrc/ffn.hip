@@ -38,9 +38,33 @@
 
 namespace beam {
 
-constexpr int kBKS = 32;     // k per pipeline stage (one MFMA k)
-constexpr int kNW = 4;       // waves per workgroup
-constexpr int kFrag = 1024;  // bytes of one 16 x 32 bf16 MFMA operand
+// Pipeline shape.  The defaults were chosen by timing on MI355X; the macros
+// only exist so that other shapes can be built for comparison.
+#ifndef BEAM_GEMM_S4
+#define BEAM_GEMM_S4 4
+#endif
+#ifndef BEAM_GEMM_S8
+#define BEAM_GEMM_S8 5
+#endif
+#ifndef BEAM_GEMM_S12
+#define BEAM_GEMM_S12 5
+#endif
+#ifndef BEAM_GEMM_MAXMB
+#define BEAM_GEMM_MAXMB 12
+#endif
+#ifndef BEAM_GEMM_NW8
+#define BEAM_GEMM_NW8 8
+#endif
+#ifndef BEAM_GEMM_NW12
+#define BEAM_GEMM_NW12 8
+#endif
+constexpr int kBKS = 32;                // k per pipeline stage (one MFMA k)
+constexpr int kFrag = 1024;             // bytes of one 16 x 32 bf16 MFMA operand
+constexpr int kFragElems = kFrag / 2;
+// Output columns of one work item: every configuration covers 128 h columns
+// (gate/up) or 256 y columns (down), so the host's item count is config-free.
+constexpr int kColsGateUp = 128;
+constexpr int kColsDown = 256;
 
 // s_waitcnt immediate (GFX9 encoding) that waits until at most n vector
 // memory operations of this wave are outstanding; other counters untouched.
@@ -52,6 +76,11 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
+}
+
+// Wait for all of this wave's LDS reads (lgkmcnt(0)); other counters untouched.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 // Compiler-level fence: no memory access moves across it (emits nothing).
@@ -101,15 +130,16 @@ struct ItemArgs {
   const uint16_t* A;
   const int32_t* gather;
   int topk;
-  const uint16_t* W;       // this expert's weight rows
+  const uint16_t* W;       // this expert's weights (row-major or fragment-packed)
   uint16_t* C;
   int K, n_out, up_row0;
+  int packed;              // 1: W is in fragment order (see pack_weights_kernel)
   int row0, nrows, ntile;
 };
 
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks.  MB sizes the
 // LDS ring; fragments of blocks NRB..MB-1 are not loaded.
-template <int NRB, int MB, int NCBW, int S, bool SWIGLU>
+template <int NRB, int MB, int kNW, int NCBW, int S, bool SWIGLU>
 __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int wave, int lane) {
   constexpr int D = S - 1;                      // stages in flight ahead of compute
   constexpr int AOFF = kNW * NCBW * kFrag;      // slot = B fragments, then A fragments
@@ -143,8 +173,13 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
     } else {
       wrow = a.ntile * WCOLS + wave * NCBW * 16 + cb * 16 + r;
     }
-    bsrc[cb] = a.W + (size_t)wrow * a.K + 8 * g;
+    // row-major: row wrow, k chunk 8g; packed: fragment (wrow/16, stage) holds
+    // this lane's 16 bytes at lane*8, and a row block's fragments follow
+    // each other along k.
+    bsrc[cb] = a.packed ? a.W + (size_t)((wrow - r) >> 4) * nk * kFragElems + lane * 8
+                        : a.W + (size_t)wrow * a.K + 8 * g;
   }
+  const int bstep = a.packed ? kFragElems : kBKS;  // elements per stage along a stream
   // LDS byte offset of the ring (addrspace cast, not the flat address)
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
@@ -155,7 +190,8 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
     const uint32_t so = (uint32_t)((st % S) * SLOT);
     const int k0 = st * kBKS;
 #pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb) lds_dma16(bsrc[cb] + k0, b_base + so + cb * kFrag);
+    for (int cb = 0; cb < NCBW; ++cb)
+      lds_dma16(bsrc[cb] + (size_t)st * bstep, b_base + so + cb * kFrag);
 #pragma unroll
     for (int j = 0; j < AMAX; ++j)
       if (j < na) lds_dma16(asrc[j] + k0, a_base + so + kNW * j * kFrag);
@@ -171,27 +207,51 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
   for (int st = 0; st < D; ++st)
     if (st < nk) issue(st);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(D - 1, nk - 1 - kt);
+  // wait until stage `st` has landed, given that stages up to
+  // min(st + D - 1, nk - 1) have been issued
+  auto wait_for = [&](int st) {
+    const int ahead = min(D - 1, nk - 1 - st);
     if (na == AMAX) wait_stage<D - 1, NCBW + AMAX>(ahead);
     else wait_stage<D - 1, NCBW + AMAX - 1>(ahead);
-    stage_barrier();  // stage kt visible to all waves; slot (kt-1)%S is free
-    if (kt + D < nk) issue(kt + D);
-    const uint8_t* sl = lds + (kt % S) * SLOT;
-    uint4 bf[NCBW], af[NRB];
+  };
+  auto read_frags = [&](int st, uint4 (&af)[NRB], uint4 (&bf)[NCBW]) {
+    const uint8_t* sl = lds + (st % S) * SLOT;
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb)
       bf[cb] = *reinterpret_cast<const uint4*>(sl + (wave * NCBW + cb) * kFrag + 16 * lane);
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
       af[i] = *reinterpret_cast<const uint4*>(sl + AOFF + i * kFrag + 16 * lane);
+  };
+  // One K-stage.  The next stage's fragments are read from LDS before this
+  // stage's MFMAs are issued, so LDS latency hides behind matrix work.  Slot
+  // reuse: stage kt + D refills the slot of stage kt - 1, whose fragments
+  // every wave read (and waited for) before the previous barrier.
+  auto step = [&](int kt, uint4 (&ca)[NRB], uint4 (&cbf)[NCBW], uint4 (&na_)[NRB],
+                  uint4 (&nb_)[NCBW]) {
+    if (kt + D < nk) issue(kt + D);
+    if (kt + 1 < nk) wait_for(kt + 1);
+    wait_lgkm0();      // this wave's reads of stage kt have landed
+    stage_barrier();   // stage kt + 1 is visible to every wave
+    if (kt + 1 < nk) read_frags(kt + 1, na_, nb_);
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int cb = 0; cb < NCBW; ++cb)
-        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bf[cb]),
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[i]), as_bf16x8(cbf[cb]),
                                                              acc[i][cb], 0, 0, 0);
+  };
+
+  uint4 a0[NRB], b0[NCBW], a1[NRB], b1[NCBW];
+  wait_for(0);
+  stage_barrier();
+  read_frags(0, a0, b0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, a0, b0, a1, b1);
+    step(kt + 1, a1, b1, a0, b0);
   }
+  if (kt < nk) step(kt, a0, b0, a1, b1);
   stage_barrier();  // every wave is done with the ring before the next item refills it
 
   // epilogue: lane holds rows 4g..4g+3 of column r of each 16x16 block
@@ -216,24 +276,25 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
   }
 }
 
-template <int N, int MB, int NCBW, int S, bool SWIGLU>
+template <int N, int MB, int kNW, int NCBW, int S, bool SWIGLU>
 __device__ __forceinline__ void gemm_item_dispatch(int nrb, const ItemArgs& a, uint8_t* lds,
                                                    int wave, int lane) {
   if constexpr (N > MB) {
     return;
   } else {
-    if (nrb == N) gemm_item<N, MB, NCBW, S, SWIGLU>(a, lds, wave, lane);
-    else gemm_item_dispatch<N + 1, MB, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
+    if (nrb == N) gemm_item<N, MB, kNW, NCBW, S, SWIGLU>(a, lds, wave, lane);
+    else gemm_item_dispatch<N + 1, MB, kNW, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
   }
 }
 
-template <int MB, int NCBW, int S, bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void stream_gemm_kernel(
+template <int MB, int kNW, int NCBW, int S, bool SWIGLU>
+__global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0) {
+    const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed) {
   constexpr int SLOT = (kNW * NCBW + MB) * kFrag;
   constexpr int WCOLS = kNW * (SWIGLU ? NCBW / 2 : NCBW) * 16;
+  static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S * SLOT];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -251,10 +312,10 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(
     if (q >= total) break;
     const int tile = q / nt_n;
     const int e = plan_expert[tile];
-    ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0,
+    ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0, packed,
                plan_row0[tile], plan_rows[tile], q - tile * nt_n};
     const int nrb = (a.nrows + 15) >> 4;
-    gemm_item_dispatch<1, MB, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
+    gemm_item_dispatch<1, MB, kNW, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
   }
 }
 
@@ -295,23 +356,46 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* __restric
   if (e == 255) plan[0] = min(sc[255], max_tiles);
 }
 
-// ---------------------------------------------------------------------------
-// Launch configurations: (MB, NCBW, S).  LDS per workgroup = S * (16 + MB) KB.
-constexpr int kNCBW = 4;
+// Fragment packing: expert e's [N, K] row-major matrix is rewritten as
+// [N/16][K/32][64 lanes][8] -- the 1 KB MFMA operand of rows 16b..16b+15 and
+// k 32s..32s+31, lane l holding row 16b + l%16, k 32s + 8(l/16) .. +7.  A row
+// block's fragments are contiguous along k, so a weight stream reads whole
+// kilobytes from consecutive addresses.  One thread moves 16 bytes.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ src,
+                                                           uint16_t* __restrict__ dst, int N,
+                                                           int K, int64_t chunks) {
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-element chunk of dst
+  if (d >= chunks) return;
+  const int64_t per_expert = (int64_t)N * K / 8;
+  const int64_t e = d / per_expert;
+  const int64_t f = d - e * per_expert;
+  const int lane = (int)(f & 63);
+  const int64_t frag = f >> 6;
+  const int nk = K / kBKS;
+  const int64_t blk = frag / nk;
+  const int st = (int)(frag - blk * nk);
+  const int64_t row = blk * 16 + (lane & 15);
+  const int64_t k = (int64_t)st * kBKS + (lane >> 4) * 8;
+  st16(dst + d * 8, ld16(src + e * (int64_t)N * K + row * K + k));
+}
 
-template <int MB, int S, bool SWIGLU>
+// ---------------------------------------------------------------------------
+// Launch configurations (MB, waves, NCBW, S).  LDS per workgroup =
+// S * (waves * NCBW + MB) KB.  Small m-tiles use 4 waves and fit two
+// workgroups per CU; large ones use 8 waves (two per SIMD) in one workgroup.
+template <int MB, int NW, int NCBW, int S, bool SWIGLU>
 static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int topk,
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                                int64_t max_items, hipStream_t stream) {
-  auto kern = stream_gemm_kernel<MB, kNCBW, S, SWIGLU>;
+                                int packed, int64_t max_items, hipStream_t stream) {
+  auto kern = stream_gemm_kernel<MB, NW, NCBW, S, SWIGLU>;
   static int per_cu = 0;  // resident workgroups per CU, fixed per build
   static int cus = 0;
   if (per_cu == 0) {
     int dev = 0, n = 0, occ = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err == hipSuccess) err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0);
+    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, NW * 64, 0);
     if (err != hipSuccess) return err;
     cus = n;
     per_cu = occ > 0 ? occ : 1;
@@ -321,8 +405,8 @@ static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int to
   if (cap < grid) grid = cap;
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, A, gather, topk, W, wstride,
-                     C, plan, max_tiles, K, n_out, up_row0);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, stream, A, gather, topk, W,
+                     wstride, C, plan, max_tiles, K, n_out, up_row0, packed);
   return hipGetLastError();
 }
 
@@ -334,11 +418,11 @@ int ffn_rows_per_tile(int mb) { return 16 * mb; }
 int ffn_choose_mb(int64_t rows, int E) {
   const int64_t mean = rows / (E > 0 ? E : 1);
   if (mean <= 40) return 4;
-  if (mean <= 80) return 8;
+  if (mean <= 80 || BEAM_GEMM_MAXMB == 8) return 8;
   return 12;
 }
 
-int ffn_out_cols_per_item(bool swiglu) { return kNW * (swiglu ? kNCBW / 2 : kNCBW) * 16; }
+int ffn_out_cols_per_item(bool swiglu) { return swiglu ? kColsGateUp : kColsDown; }
 
 hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* plan, int max_tiles,
                             hipStream_t stream) {
@@ -347,20 +431,33 @@ hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* pl
   return hipGetLastError();
 }
 
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N, int K,
+                               hipStream_t stream) {
+  const int64_t chunks = (int64_t)E * N * K / 8;
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst,
+                     N, K, chunks);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                               int64_t max_items, hipStream_t stream) {
-#define BEAM_STREAM_CASE(MBV, SV)                                                               \
+                               int packed, int64_t max_items, hipStream_t stream) {
+#define BEAM_STREAM_CASE(MBV, NWV, NCBWV, SV)                                                   \
   case MBV:                                                                                     \
-    return swiglu ? launch_stream<MBV, SV, true>(A, gather, topk, W, wstride, C, plan,          \
-                                                 max_tiles, K, n_out, up_row0, max_items, stream) \
-                  : launch_stream<MBV, SV, false>(A, gather, topk, W, wstride, C, plan,         \
-                                                  max_tiles, K, n_out, up_row0, max_items, stream);
+    return swiglu ? launch_stream<MBV, NWV, NCBWV, SV, true>(A, gather, topk, W, wstride, C,    \
+                                                             plan, max_tiles, K, n_out,         \
+                                                             up_row0, packed, max_items,        \
+                                                             stream)                            \
+                  : launch_stream<MBV, NWV, NCBWV, SV, false>(A, gather, topk, W, wstride, C,   \
+                                                              plan, max_tiles, K, n_out,        \
+                                                              up_row0, packed, max_items,       \
+                                                              stream);
   switch (mb) {
-    BEAM_STREAM_CASE(4, 4)
-    BEAM_STREAM_CASE(8, 5)
-    BEAM_STREAM_CASE(12, 5)
+    BEAM_STREAM_CASE(4, 4, 4, BEAM_GEMM_S4)
+    BEAM_STREAM_CASE(8, BEAM_GEMM_NW8, 16 / BEAM_GEMM_NW8, BEAM_GEMM_S8)
+    BEAM_STREAM_CASE(12, BEAM_GEMM_NW12, 16 / BEAM_GEMM_NW12, BEAM_GEMM_S12)
     default:
       return hipErrorInvalidValue;
   }

@@ -28,7 +28,9 @@ hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* pl
 hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                               int64_t max_items, hipStream_t stream);
+                               int packed, int64_t max_items, hipStream_t stream);
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N, int K,
+                               hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
                           uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream);

@@ -76,7 +76,18 @@ typedef struct moe_config {
   int32_t renormalize;    /* 1: combine weight = score / sum of the topk chosen
                              scores ("normalized router weights"); 0: raw score   */
   float routed_scaling;   /* factor applied to the combined output, 2.5          */
+  int32_t weight_layout;  /* expert weight storage: MOE_LAYOUT_ROW_MAJOR or
+                             MOE_LAYOUT_PACKED (written by moe_pack_weights)     */
 } moe_config_t;
+
+/* Expert weight layouts. */
+enum moe_weight_layout {
+  MOE_LAYOUT_ROW_MAJOR = 0,  /* w_gate_up [E, 2I, H], w_down [E, H, I], row-major    */
+  MOE_LAYOUT_PACKED = 1      /* same sizes, each expert's [N, K] matrix stored as
+                                [N/16][K/32][64][8]: the 16 x 32 bf16 operand tiles of
+                                the gfx950 matrix cores, lane-ordered, consecutive
+                                along K (see moe_pack_weights)                        */
+};
 
 /* Bytes of workspace `entry` needs for `cfg` (written to *bytes). */
 int moe_workspace_bytes(const moe_config_t* cfg, int entry, size_t* bytes);
@@ -129,6 +140,7 @@ int moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* count
  *   perm_src   [T*topk] int32, offsets [E + 1] int32 (from moe_permute)
  *   w_gate_up  [E, 2*I, H] bf16: rows [0, I) gate, rows [I, 2I) up
  *   w_down     [E, H, I] bf16
+ *   (both in cfg->weight_layout)
  *   y_perm     [T*topk, H] bf16 out, expert-major row order
  * Experts with no rows read no weights.
  */
@@ -170,6 +182,17 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
                       const float* sel_bias, const uint16_t* w_gate_up, const uint16_t* w_down,
                       uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Rewrites expert weights from MOE_LAYOUT_ROW_MAJOR into MOE_LAYOUT_PACKED
+ * (a pure permutation of each expert's elements; run once at load time).
+ *   w_gate_up, w_down            row-major inputs (shapes as above)
+ *   packed_gate_up, packed_down  outputs of the same sizes; must not overlap
+ *                                the inputs
+ * Either pair may be NULL to skip it.  num_tokens is ignored.
+ */
+int moe_pack_weights(const moe_config_t* cfg, const uint16_t* w_gate_up, const uint16_t* w_down,
+                     uint16_t* packed_gate_up, uint16_t* packed_down, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* moe_status_string(int status);

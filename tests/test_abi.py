@@ -34,7 +34,8 @@ def test_status_strings():
 def _cfg(**kw):
     base = dict(num_tokens=64, hidden=256, intermediate=128)
     base.update(kw)
-    return gtr.make_config(base.pop("num_tokens"), base.pop("hidden"), base.pop("intermediate"), **base)
+    return gtr.make_config(base.pop("num_tokens"), base.pop("hidden"), base.pop("intermediate"),
+                           **base)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -137,3 +138,21 @@ def test_python_binding_requires_device_tensors():
     x = torch.zeros(4, 256, dtype=torch.bfloat16)
     with pytest.raises((ValueError, TypeError)):
         gtr.route(x, torch.zeros(256, 256))
+
+
+def test_weight_layout_and_pack_validation():
+    cfg = _cfg(weight_layout=2)
+    n = ctypes.c_size_t(0)
+    lib = gtr.lib()
+    assert lib.moe_workspace_bytes(ctypes.byref(cfg), L.ENTRY_LAYER, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
+    cfg = _cfg()
+    B = ctypes.c_void_p(0x100000000)
+    # one side of a pair missing
+    assert lib.moe_pack_weights(ctypes.byref(cfg), A, None, None, None, None) == L.MOE_ERR_INVALID_ARG
+    # misaligned
+    assert lib.moe_pack_weights(ctypes.byref(cfg), MIS, None, B, None, None) == L.MOE_ERR_INVALID_ARG
+    # output overlapping the input
+    assert lib.moe_pack_weights(ctypes.byref(cfg), A, None, ctypes.c_void_p(0x10000 + 4096), None,
+                                None) == L.MOE_ERR_INVALID_ARG
+    # nothing to do
+    assert lib.moe_pack_weights(ctypes.byref(cfg), None, None, None, None, None) == L.MOE_OK

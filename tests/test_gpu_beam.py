@@ -29,8 +29,10 @@ def beam():
     say("[beam] generating router and 256 experts on the device")
     wr = synth.make_router(w, 0, DEV)
     wgu, wd = synth.make_experts(w, 0, DEV)
+    pgu, pd = gtr.pack_weights(wgu, wd)
     torch.cuda.synchronize()
-    return {"w_router": wr, "w_gate_up": wgu, "w_down": wd, "wr_np": to_np(wr)}
+    return {"w_router": wr, "w_gate_up": wgu, "w_down": wd, "wr_np": to_np(wr),
+            "p_gate_up": pgu, "p_down": pd}
 
 
 def _expert_np(beam, e):
@@ -47,6 +49,10 @@ def test_beam_layer(beam, name):
                                       return_routing=True)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    # the fragment-packed weights give the same bits
+    outp = gtr.layer_forward(x, beam["w_router"], beam["p_gate_up"], beam["p_down"],
+                             weight_layout=gtr.LAYOUT_PACKED)
+    assert torch.equal(out, outp)
     xn = to_np(x)
     say(f"[beam:{name}] oracle routing")
     rr = oracle.route(xn, beam["wr_np"])
@@ -96,8 +102,8 @@ def test_beam_staged_calls_match_layer(beam):
     out = gtr.layer_forward(x, beam["w_router"], beam["w_gate_up"], beam["w_down"])
     ids, wt = gtr.route(x, beam["w_router"])
     c, o, ps, pd = gtr.permute(ids)
-    h = gtr.expert_gate_up(x, ps, o, beam["w_gate_up"])
-    y = gtr.expert_down(h, o, beam["w_down"])
+    h = gtr.expert_gate_up(x, ps, o, beam["p_gate_up"], weight_layout=gtr.LAYOUT_PACKED)
+    y = gtr.expert_down(h, o, beam["p_down"], weight_layout=gtr.LAYOUT_PACKED)
     out2 = gtr.combine(y, pd, wt)
     assert torch.equal(out, out2)
     y2 = gtr.expert_ffn(x, ps, o, beam["w_gate_up"], beam["w_down"])

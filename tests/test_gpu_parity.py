@@ -244,3 +244,35 @@ def test_layer_on_side_stream(tiny):
     torch.cuda.current_stream(DEV).wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+# ------------------------------------------------------------ packed layout
+def test_pack_weights_is_the_documented_permutation(tiny):
+    say("[pack] tiny weights")
+    pgu, pd = gtr.pack_weights(tiny["w_gate_up"], tiny["w_down"])
+    for W, P in ((tiny["w_gate_up"], pgu), (tiny["w_down"], pd)):
+        E, N, K = W.shape
+        w = W.view(torch.int16).cpu().numpy()
+        p = P.view(torch.int16).cpu().numpy().reshape(E, N // 16, K // 32, 64, 8)
+        lane = np.arange(64)
+        for e in (0, 17, 255):
+            for b in (0, N // 16 - 1):
+                for s in (0, K // 32 - 1):
+                    rows = 16 * b + lane % 16
+                    cols = 32 * s + 8 * (lane // 16)
+                    ref = np.stack([w[e, rows, cols + j] for j in range(8)], axis=1)
+                    assert np.array_equal(p[e, b, s], ref)
+        # a permutation: same multiset of values
+        assert np.array_equal(np.sort(w.ravel()), np.sort(P.view(torch.int16).cpu().numpy().ravel()))
+
+
+@pytest.mark.parametrize("T", [64, 128, 700, 2048])
+def test_packed_layout_matches_row_major_bitwise(tiny, T):
+    # same operands, same k order: the packed path must reproduce the row-major
+    # path bit for bit at every m-tile height
+    say(f"[pack] layer T={T}")
+    pgu, pd = gtr.pack_weights(tiny["w_gate_up"], tiny["w_down"])
+    x = synth.make_x(synth.workload("tiny", T=T), 5, DEV)
+    a = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
+    b = gtr.layer_forward(x, tiny["w_router"], pgu, pd, weight_layout=gtr.LAYOUT_PACKED)
+    assert torch.equal(a, b)
