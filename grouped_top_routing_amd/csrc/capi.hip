@@ -52,7 +52,8 @@ int64_t max_tiles_for(const moe_config_t* c) {
 }
 
 size_t route_ws(const moe_config_t* c) {
-  return align_up((size_t)c->num_tokens * c->num_experts * sizeof(float));
+  return align_up((size_t)router_splits(c->num_tokens, c->hidden) * c->num_tokens *
+                  c->num_experts * sizeof(float));
 }
 size_t permute_ws(const moe_config_t* c) {
   const int64_t nchunks = (pairs(c) + kChunk - 1) / kChunk;
@@ -107,11 +108,12 @@ int device_ready() {
 int do_route(const moe_config_t* c, const uint16_t* x, const float* wr, const float* bias,
              int32_t* ids, float* w, void* scratch, hipStream_t s) {
   const int T = (int)c->num_tokens;
-  float* logits = static_cast<float*>(scratch);
-  int st = hip_status(launch_router_logits(x, wr, logits, T, c->hidden, c->num_experts, s));
+  float* part = static_cast<float*>(scratch);
+  const int splits = router_splits(T, c->hidden);
+  int st = hip_status(launch_router_logits(x, wr, part, T, c->hidden, splits, s));
   if (st) return st;
-  return hip_status(launch_select(logits, bias, ids, w, T, c->num_groups, c->topk_groups, c->topk,
-                                  c->renormalize, s));
+  return hip_status(launch_select(part, splits, bias, ids, w, T, c->num_groups, c->topk_groups,
+                                  c->topk, c->renormalize, s));
 }
 
 int do_permute(const moe_config_t* c, const int32_t* ids, int32_t* counts, int32_t* offsets,
@@ -213,12 +215,13 @@ int moe_route_replay(const moe_config_t* cfg, const uint16_t* x, const float* w_
   if (cfg->num_tokens == 0) return MOE_OK;
   if ((st = device_ready())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* logits = static_cast<float*>(workspace);
+  float* part = static_cast<float*>(workspace);
   const int T = (int)cfg->num_tokens;
-  st = hip_status(launch_router_logits(x, w_router, logits, T, cfg->hidden, cfg->num_experts, s));
+  const int splits = router_splits(T, cfg->hidden);
+  st = hip_status(launch_router_logits(x, w_router, part, T, cfg->hidden, splits, s));
   if (st) return st;
-  return hip_status(
-      launch_replay(logits, topk_ids, topk_w, T, cfg->num_experts, cfg->topk, cfg->renormalize, s));
+  return hip_status(launch_replay(part, splits, topk_ids, topk_w, T, cfg->num_experts, cfg->topk,
+                                  cfg->renormalize, s));
 }
 
 int moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts,

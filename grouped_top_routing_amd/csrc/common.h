@@ -39,4 +39,66 @@ __device__ __forceinline__ float sigmoidf_(float v) {
   return 1.0f / (1.0f + expf(-v));
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS streaming (used by the expert GEMMs and the router).
+// s_waitcnt immediate (GFX9 encoding) that waits until at most n vector
+// memory operations of this wave are outstanding; other counters untouched.
+__host__ __device__ constexpr int vm_wait_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
+}
+
+// Wait for all of this wave's LDS reads (lgkmcnt(0)); other counters untouched.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Compiler-level fence: no memory access moves across it (emits nothing).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding direct load).
+__device__ __forceinline__ void stage_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+template <int AHEAD, int L>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  // wait until only `ahead` later stages (L loads each) remain in flight
+  if constexpr (AHEAD == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= AHEAD) wait_vm<AHEAD * L>();
+    else wait_stage<AHEAD - 1, L>(ahead);
+  }
+}
+
+// One direct global -> LDS load: lane l's 16 bytes at `g` land at LDS byte
+// address lds_addr + 16*l (lds_addr must be wave-uniform; it goes in M0).
+// Issued from inline asm so the compiler's own wait-count pass does not see
+// it: the pass would otherwise put a vmcnt(0) -- a full drain of the ring --
+// before every later LDS read.  Completion is tracked by hand with
+// wait_vm<>() (vector memory operations of a wave complete in order).  M0 is
+// saved and restored, and s_nop covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);  // free when already uniform
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_addr)
+      : "memory");
+}
+
 }  // namespace beam

@@ -8,13 +8,14 @@ namespace beam {
 
 constexpr int kChunk = 4096;  // (token, slot) pairs per permute workgroup
 
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* logits, int T, int H,
-                                int E, hipStream_t stream);
-hipError_t launch_select(const float* logits, const float* sel_bias, int32_t* ids, float* w,
-                         int T, int G, int topk_groups, int topk, int renormalize,
+int router_splits(int64_t T, int H);
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H,
+                                int splits, hipStream_t stream);
+hipError_t launch_select(const float* part, int splits, const float* sel_bias, int32_t* ids,
+                         float* w, int T, int G, int topk_groups, int topk, int renormalize,
                          hipStream_t stream);
-hipError_t launch_replay(const float* logits, const int32_t* ids, float* w, int T, int E,
-                         int topk, int renormalize, hipStream_t stream);
+hipError_t launch_replay(const float* part, int splits, const int32_t* ids, float* w, int T,
+                         int E, int topk, int renormalize, hipStream_t stream);
 
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int32_t* counts, int32_t* offsets,
                           int32_t* perm_src, int32_t* perm_dst, int32_t* chunk_hist,

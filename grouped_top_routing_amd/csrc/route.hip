@@ -9,10 +9,11 @@
 // stay FP32).
 //
 // Two kernels:
-//   router_logits_kernel  logits[T, 256] = x . W_r^T on the fp32 matrix cores
-//                         (v_mfma_f32_16x16x4_f32): products and sums are true
-//                         fp32, bf16 activations are widened exactly.
-//   select_kernel<G>      one wavefront per token: sigmoid, group top-two sums
+//   router_logits_kernel  k-split partial logits x . W_r^T on the bf16 matrix
+//                         cores with an exact three-way bf16 split of the fp32
+//                         weights (fp32 products, fp32 accumulation).
+//   select_kernel<G>      one wavefront per token: sums the partials, sigmoid,
+//                         group top-two sums
 //                         by butterfly shuffles, group ranking, then topk
 //                         rounds of a wavefront-wide arg-max; writes ids and
 //                         combine weights.
@@ -22,63 +23,153 @@
 namespace beam {
 
 // ---------------------------------------------------------------------------
-// logits tile: 64 tokens x 64 experts per workgroup, 4 waves; wave w owns the
-// 16 experts [16w, 16w + 16) of the tile and all 64 tokens (4 row blocks).
-// K advances by 32 per step: lane (r = lane % 16, g = lane / 16) holds the 8
-// consecutive k values [8g, 8g + 8) of its token rows and of its expert row;
-// MFMA m (m = 0..7) consumes the m-th of them, so lane group g always supplies
-// the same k to both operands.
+// Logits on the bf16 matrix cores, fp32-exact.
+//
+// Every fp32 router weight w splits exactly into three bf16 values by
+// truncation: hi = w with its low 16 bits cleared, mid likewise from w - hi,
+// lo = w - hi - mid (at most 8 significant bits left, so it is a bf16 value).
+// The activations are bf16, so each product x*hi, x*mid, x*lo is exact in the
+// fp32 accumulator of v_mfma_f32_16x16x32_bf16, and logit = sum over k of
+// x*hi + x*mid + x*lo is an fp32-accumulated dot product of the exact fp32
+// weights -- at a third of the bf16 rate, ~5x the fp32 matrix rate.
+//
+// Tile: 128 tokens x 256 experts per workgroup, k split over blockIdx.y (the
+// partial sums are added in split order by select_kernel, so results do not
+// depend on the grid).  Wave w owns experts [64w, 64w + 64) and all 128
+// tokens.  x fragments (16 tokens x 32 k, MFMA lane order) stream into an LDS
+// ring with direct loads shared by the 4 waves; each wave's weights go
+// straight to registers (no other wave needs them), both kRD stages ahead.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_logits_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ logits,
-    int T, int H, int E) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int t0 = blockIdx.x * 64;
-  const int e = blockIdx.y * 64 + wave * 16 + r;
+constexpr int kRT = 128;              // tokens per workgroup
+constexpr int kRB = kRT / 16;         // token row blocks
+constexpr int kRD = 3;                // stages in flight
+constexpr int kRS = kRD + 1;          // LDS ring slots
+constexpr int kRL = 2 + 8;            // loads per wave per stage: 2 x fragments + 4 experts x 32 B
 
-  const float* wrow = wr + (size_t)e * H + 8 * g;
-  const uint16_t* xrow[4];
+__device__ __forceinline__ uint32_t hi16(uint32_t u) { return u & 0xffff0000u; }
+
+// Three bf16x8 operands (hi, mid, lo) from 8 fp32 weights held in two uint4.
+__device__ __forceinline__ void split3(const uint4& w0, const uint4& w1, bf16x8_t& ph,
+                                       bf16x8_t& pm, bf16x8_t& pl) {
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t h[8], m[8], l[8];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    int t = t0 + rb * 16 + r;
-    t = t < T ? t : T - 1;  // clamp: rows past T are computed but never stored
-    xrow[rb] = x + (size_t)t * H + 8 * g;
+  for (int i = 0; i < 8; ++i) {
+    h[i] = hi16(w[i]);
+    const float r1 = __uint_as_float(w[i]) - __uint_as_float(h[i]);
+    m[i] = hi16(__float_as_uint(r1));
+    l[i] = __float_as_uint(r1 - __uint_as_float(m[i]));  // low 16 bits are zero
   }
+  uint4 H, M, L;
+  H.x = (h[0] >> 16) | h[1]; H.y = (h[2] >> 16) | h[3]; H.z = (h[4] >> 16) | h[5]; H.w = (h[6] >> 16) | h[7];
+  M.x = (m[0] >> 16) | m[1]; M.y = (m[2] >> 16) | m[3]; M.z = (m[4] >> 16) | m[5]; M.w = (m[6] >> 16) | m[7];
+  L.x = (l[0] >> 16) | l[1]; L.y = (l[2] >> 16) | l[3]; L.z = (l[4] >> 16) | l[5]; L.w = (l[6] >> 16) | l[7];
+  ph = as_bf16x8(H);
+  pm = as_bf16x8(M);
+  pl = as_bf16x8(L);
+}
 
-  f32x4_t acc[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+__global__ __launch_bounds__(256, 1) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ part,
+    int T, int H, int kchunk) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRS * kRB * 1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * kRT;
+  const int kbeg = blockIdx.y * kchunk;
+  const int nk = kchunk / 32;
 
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    const float4 w0 = *reinterpret_cast<const float4*>(wrow + k0);
-    const float4 w1 = *reinterpret_cast<const float4*>(wrow + k0 + 4);
-    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    uint4 xv[4];
+  // x fragments this wave loads: row blocks wave and wave + 4
+  const uint16_t* xsrc[2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) xv[rb] = ld16(xrow[rb] + k0);
+  for (int j = 0; j < 2; ++j) {
+    int t = t0 + (wave + 4 * j) * 16 + r;
+    t = t < T ? t : T - 1;  // rows past T repeat the last token (computed, never stored)
+    xsrc[j] = x + (size_t)t * H + kbeg + 8 * g;
+  }
+  // weight rows of this lane: expert 64*wave + 16*cb + r, k chunk 8g
+  const float* wsrc[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const uint32_t xw[4] = {xv[rb].x, xv[rb].y, xv[rb].z, xv[rb].w};
+  for (int cb = 0; cb < 4; ++cb) wsrc[cb] = wr + (size_t)(64 * wave + 16 * cb + r) * H + kbeg + 8 * g;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
+
+  uint4 wreg[kRD][4][2];
+  auto issue = [&](int st, uint4 (&wr_)[4][2]) {
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((st % kRS) * kRB * 1024));
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const uint32_t half = (m & 1) ? (xw[m >> 1] >> 16) : (xw[m >> 1] & 0xffffu);
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_to_f32(half), wv[m], acc[rb], 0, 0, 0);
+    for (int j = 0; j < 2; ++j) lds_dma16(xsrc[j] + st * 32, sl + (wave + 4 * j) * 1024);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      wr_[cb][0] = ld16(wsrc[cb] + st * 32);
+      wr_[cb][1] = ld16(wsrc[cb] + st * 32 + 4);
+    }
+  };
+
+  f32x4_t acc[kRB][4];
+#pragma unroll
+  for (int i = 0; i < kRB; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < kRD; ++st)
+    if (st < nk) issue(st, wreg[st]);
+
+  // one stage: consume register set `cur`, then refill it with stage kt + kRD
+  auto step = [&](int kt, uint4 (&cur)[4][2]) {
+    wait_stage<kRD - 1, kRL>(min(kRD - 1, nk - 1 - kt));
+    stage_barrier();
+    const uint8_t* sl = lds + (kt % kRS) * kRB * 1024;
+    bf16x8_t bh[4], bm[4], bl[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) split3(cur[cb][0], cur[cb][1], bh[cb], bm[cb], bl[cb]);
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(sl + i * 1024 + 16 * lane));
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[cb], acc[i][cb], 0, 0, 0);
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[cb], acc[i][cb], 0, 0, 0);
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[cb], acc[i][cb], 0, 0, 0);
       }
     }
+    wait_lgkm0();
+    if (kt + kRD < nk) issue(kt + kRD, cur);
+  };
+  int kt = 0;
+  for (; kt + kRD <= nk; kt += kRD) {
+#pragma unroll
+    for (int j = 0; j < kRD; ++j) step(kt + j, wreg[j]);
   }
+#pragma unroll
+  for (int j = 0; j < kRD; ++j)
+    if (kt + j < nk) step(kt + j, wreg[j]);
 
-  // D layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column r.
+  // D layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column r
+  float* out = part + (size_t)blockIdx.y * T * 256;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int i = 0; i < kRB; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + rb * 16 + 4 * g + i;
-      if (t < T) logits[(size_t)t * E + e] = acc[rb][i];
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + i * 16 + 4 * g + v;
+      if (t < T) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) out[(size_t)t * 256 + 64 * wave + 16 * cb + r] = acc[i][cb][v];
+      }
     }
-  }
+}
+
+// k splits for the logits: enough workgroups to cover the GPU (~512), each
+// split a whole number of 32-wide k steps.
+int router_splits(int64_t T, int H) {
+  const int64_t tiles = (T + kRT - 1) / kRT;
+  const int steps = H / 32;
+  int want = (int)((512 + tiles - 1) / (tiles > 0 ? tiles : 1));
+  if (want > steps) want = steps;
+  int best = 1;
+  for (int s = 1; s <= want; ++s)
+    if (steps % s == 0) best = s;
+  return best;
 }
 
 // ---------------------------------------------------------------------------
@@ -92,9 +183,21 @@ __device__ __forceinline__ float pick4(const float (&v)[4], int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
+// Sum of the k-split partial logits of token t, experts 4*lane .. 4*lane+3,
+// added in split order.
+__device__ __forceinline__ void gather_logits(const float* __restrict__ part, int splits, int T,
+                                              int t, int lane, float (&lg)[4]) {
+  float4 a = *reinterpret_cast<const float4*>(part + (size_t)t * 256 + 4 * lane);
+  for (int s = 1; s < splits; ++s) {
+    const float4 b = *reinterpret_cast<const float4*>(part + ((size_t)s * T + t) * 256 + 4 * lane);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  lg[0] = a.x; lg[1] = a.y; lg[2] = a.z; lg[3] = a.w;
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void select_kernel(
-    const float* __restrict__ logits, const float* __restrict__ sel_bias,
+    const float* __restrict__ part, int splits, const float* __restrict__ sel_bias,
     int32_t* __restrict__ ids, float* __restrict__ wout, int T, int topk_groups, int topk,
     int renormalize) {
   constexpr int LPG = kWave / G;  // lanes per group (group = 4 * LPG experts)
@@ -102,8 +205,8 @@ __global__ __launch_bounds__(256) void select_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
 
-  const float4 lv = *reinterpret_cast<const float4*>(logits + (size_t)t * 256 + 4 * lane);
-  const float lg[4] = {lv.x, lv.y, lv.z, lv.w};
+  float lg[4];
+  gather_logits(part, splits, T, t, lane, lg);
   float s[4], sel[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -175,8 +278,8 @@ __global__ __launch_bounds__(256) void select_kernel(
 
 // Routing replay: scores of caller-given experts, weights only.
 __global__ __launch_bounds__(256) void replay_kernel(
-    const float* __restrict__ logits, const int32_t* __restrict__ ids, float* __restrict__ wout,
-    int T, int E, int topk, int renormalize) {
+    const float* __restrict__ part, int splits, const int32_t* __restrict__ ids,
+    float* __restrict__ wout, int T, int E, int topk, int renormalize) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -184,7 +287,9 @@ __global__ __launch_bounds__(256) void replay_kernel(
   if (lane < topk) {
     int e = ids[(size_t)t * topk + lane];
     e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    my_s = sigmoidf_(logits[(size_t)t * E + e]);
+    float lg = 0.f;
+    for (int s = 0; s < splits; ++s) lg += part[((size_t)s * T + t) * E + e];
+    my_s = sigmoidf_(lg);
   }
   float ssum = 0.f;
   for (int j = 0; j < topk; ++j) ssum += __shfl(my_s, j);
@@ -192,21 +297,22 @@ __global__ __launch_bounds__(256) void replay_kernel(
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* logits, int T, int H,
-                                int E, hipStream_t stream) {
-  dim3 grid((T + 63) / 64, E / 64);
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, wr, logits, T, H, E);
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H,
+                                int splits, hipStream_t stream) {
+  dim3 grid((T + kRT - 1) / kRT, splits);
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, wr, part, T, H,
+                     H / splits);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* logits, const float* sel_bias, int32_t* ids, float* w,
-                         int T, int G, int topk_groups, int topk, int renormalize,
+hipError_t launch_select(const float* part, int splits, const float* sel_bias, int32_t* ids,
+                         float* w, int T, int G, int topk_groups, int topk, int renormalize,
                          hipStream_t stream) {
   dim3 grid((T + 3) / 4);
 #define BEAM_SELECT_CASE(GV)                                                                   \
   case GV:                                                                                     \
-    hipLaunchKernelGGL(select_kernel<GV>, grid, dim3(256), 0, stream, logits, sel_bias, ids, w, \
-                       T, topk_groups, topk, renormalize);                                     \
+    hipLaunchKernelGGL(select_kernel<GV>, grid, dim3(256), 0, stream, part, splits, sel_bias,  \
+                       ids, w, T, topk_groups, topk, renormalize);                            \
     break;
   switch (G) {
     BEAM_SELECT_CASE(1)
@@ -223,10 +329,10 @@ hipError_t launch_select(const float* logits, const float* sel_bias, int32_t* id
   return hipGetLastError();
 }
 
-hipError_t launch_replay(const float* logits, const int32_t* ids, float* w, int T, int E,
-                         int topk, int renormalize, hipStream_t stream) {
-  hipLaunchKernelGGL(replay_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, ids, w, T, E,
-                     topk, renormalize);
+hipError_t launch_replay(const float* part, int splits, const int32_t* ids, float* w, int T,
+                         int E, int topk, int renormalize, hipStream_t stream) {
+  hipLaunchKernelGGL(replay_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, part, splits, ids, w,
+                     T, E, topk, renormalize);
   return hipGetLastError();
 }
 
