@@ -40,6 +40,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-experts", type=int, default=12,
                    help="experts whose rows the CPU oracle processes in its timed sample")
+    p.add_argument("--no-row-major-ref", action="store_true",
+                   help="skip the reference timing with row-major weights (profiling runs)")
+    p.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                   help="run one device-to-device copy of this size first (a known byte "
+                        "count for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -48,6 +53,27 @@ def git_sha():
         return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
                               text=True, timeout=10).stdout.strip() or None
     except Exception:
+        return None
+
+
+PROFILE = os.path.join(ROOT, "profiles", "gate_up_grouped_gemm_prefill_T4096.md")
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading for
+    a 1 GiB copy), or None when the kernel source changed since they were
+    taken or the summary is missing."""
+    import hashlib
+    try:
+        text = open(PROFILE).read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        src = b"".join(open(os.path.join(ROOT, "grouped_top_routing_amd", "csrc", f), "rb").read()
+                       for f in ("ffn.hip", "common.h"))
+        if hashlib.sha256(src).hexdigest() != blob["kernel_source_sha256"]:
+            return None
+        return int(blob["gate_up"]["read_bytes"] + blob["gate_up"]["write_bytes"])
+    except (OSError, IndexError, KeyError, ValueError):
         return None
 
 
@@ -117,7 +143,8 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
         torch.cuda.synchronize()
         return (time.perf_counter() - t1) * 1e3 / steps
     layer_ms = time_layer(wgu, wd, lay)
-    rowmajor_ms = time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR)
+    rowmajor_ms = (None if args.no_row_major_ref else
+                   time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
             "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
             "counts": counts.cpu().numpy(), "ids": ids}
@@ -186,6 +213,13 @@ def main():
     wts["p_gate_up"], wts["p_down"] = gtr.pack_weights(wts["w_gate_up"], wts["w_down"])
     torch.cuda.synchronize()
 
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
     r = run_workload(args.workload, wts, args, args.steps, args.warmup, gtr, synth, torch)
@@ -212,13 +246,15 @@ def main():
                    "seed": args.seed},
         "roofline": {"kernel": "grouped_gemm_kernel (gate/up + SwiGLU)", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if w.name == "prefill" else None,
                      "bytes_per_launch": alg["gate_up_bytes"], "avg_launch_ms": round(gu_ms, 4)},
         "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                   "bf16_mfma_frac": round(mfma_frac, 4), "algorithmic_bytes": alg["layer_bytes"],
                   "expert_flops": alg["expert_flops"], "touched_experts": alg["touched"],
                   "layer_forward_ms": round(r["layer_forward_ms"], 4),
-                  "row_major_weights_layer_ms": round(r["row_major_layer_ms"], 4),
+                  "row_major_weights_layer_ms": (None if r["row_major_layer_ms"] is None
+                                                 else round(r["row_major_layer_ms"], 4)),
                   "weight_layout": "packed (moe_pack_weights, once at load)",
                   "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
                   "histogram": {"max": int(c.max()), "min": int(c.min()),
