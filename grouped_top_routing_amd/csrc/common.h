@@ -69,6 +69,19 @@ __device__ __forceinline__ void stage_barrier() {
   compiler_fence();
 }
 
+// wait_vm with a run-time count (a branch tree down to the immediate forms);
+// counts of 63 and more wait for at most 63.
+template <int LO = 0, int HI = 63>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  if constexpr (LO == HI) {
+    wait_vm<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vm_dyn<LO, MID>(n);
+    else wait_vm_dyn<MID + 1, HI>(n);
+  }
+}
+
 template <int AHEAD, int L>
 __device__ __forceinline__ void wait_stage(int ahead) {
   // wait until only `ahead` later stages (L loads each) remain in flight

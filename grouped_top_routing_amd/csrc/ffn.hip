@@ -195,12 +195,21 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
   if (kt < nk) step(kt, a0, b0, a1, b1);
   stage_barrier();  // every wave is done with the ring before the next item refills it
 
-  // epilogue: lane holds rows 4g..4g+3 of column r of each 16x16 block
+  // Epilogue through LDS (the ring is free after the barrier above): each
+  // wave writes its accumulators as bf16 into a row-major tile -- lane holds
+  // rows 4g..4g+3 of column r of each 16x16 block; even lanes pair up with
+  // their right neighbour for 4-byte writes -- then every thread stores whole
+  // 16-byte row segments, so each output row leaves as 256 or 512 contiguous
+  // bytes.  Rows are padded by 16 bytes so the 4 row groups of a write land
+  // on different LDS banks.
+  constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per tile row
+  static_assert(16 * NRB * TSTRIDE * 2 <= S * SLOT, "epilogue tile fits the ring");
+  uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
 #pragma unroll
     for (int j = 0; j < HALF; ++j) {
-      const int col = a.ntile * WCOLS + wave * HALF * 16 + j * 16 + r;
+      const int col = wave * HALF * 16 + j * 16 + r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = i * 16 + 4 * g + v;
@@ -211,10 +220,25 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
         } else {
           o = acc[i][j][v];
         }
-        if (row < a.nrows) a.C[(size_t)(a.row0 + row) * a.n_out + col] = (uint16_t)f32_to_bf16(o);
+        const uint32_t b = f32_to_bf16(o);
+        const uint32_t nb = __shfl_xor(b, 1);
+        if ((r & 1) == 0)
+          *reinterpret_cast<uint32_t*>(tile + row * TSTRIDE + col) = b | (nb << 16);
       }
     }
   }
+  wait_lgkm0();
+  stage_barrier();
+  constexpr int CPR = WCOLS / 8;  // 16-byte chunks per tile row
+  const int nchunks = a.nrows * CPR;
+  uint16_t* out = a.C + (size_t)a.row0 * a.n_out + a.ntile * WCOLS;
+  for (int c = wave * 64 + lane; c < nchunks; c += kNW * 64) {
+    const int row = c / CPR, cc = c - row * CPR;
+    st16(out + (size_t)row * a.n_out + cc * 8,
+         *reinterpret_cast<const uint4*>(tile + row * TSTRIDE + cc * 8));
+  }
+  wait_lgkm0();
+  stage_barrier();  // the tile is read out before the next item refills the ring
 }
 
 template <int N, int MB, int kNW, int NCBW, int S, bool SWIGLU>
