@@ -159,12 +159,14 @@ __global__ __launch_bounds__(256, 1) void router_logits_kernel(
     }
 }
 
-// k splits for the logits: enough workgroups to cover the GPU (~512), each
-// split a whole number of 32-wide k steps.
+// k splits for the logits: about 256 workgroups in all, at most 32 splits
+// (the selection kernel adds the partials), each split a whole number of
+// 32-wide k steps.
 int router_splits(int64_t T, int H) {
   const int64_t tiles = (T + kRT - 1) / kRT;
   const int steps = H / 32;
-  int want = (int)((512 + tiles - 1) / (tiles > 0 ? tiles : 1));
+  int64_t want = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  if (want > 32) want = 32;
   if (want > steps) want = steps;
   int best = 1;
   for (int s = 1; s <= want; ++s)
@@ -188,6 +190,7 @@ __device__ __forceinline__ float pick4(const float (&v)[4], int i) {
 __device__ __forceinline__ void gather_logits(const float* __restrict__ part, int splits, int T,
                                               int t, int lane, float (&lg)[4]) {
   float4 a = *reinterpret_cast<const float4*>(part + (size_t)t * 256 + 4 * lane);
+#pragma unroll 8
   for (int s = 1; s < splits; ++s) {
     const float4 b = *reinterpret_cast<const float4*>(part + ((size_t)s * T + t) * 256 + 4 * lane);
     a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
