@@ -46,7 +46,8 @@ import numpy as np
 __all__ = [
     "RouteResult", "route", "route_replay", "select", "router_logits", "sigmoid_f32",
     "permute", "expert_ffn", "ffn_rows", "combine", "layer_forward",
-    "selection_admissible", "MARGIN_TOL",
+    "selection_admissible", "MARGIN_TOL", "E4M3_MAX", "e4m3_encode", "e4m3_decode",
+    "quantize_fp8_per_channel", "dequantize_fp8",
 ]
 
 #: Selection margin under which GPU and oracle may legitimately disagree.
@@ -246,3 +247,77 @@ def selection_admissible(sel_row, gs_row, chosen, *, n_groups=8, topk_groups=4, 
             continue
         return True
     return False
+
+
+# ---------------------------------------------------------------------------
+# FP8 per-channel expert weights ("Beam-1.0-501B-A23B" vLLM recipe, FP8
+# variant: FP8 per-channel weights, with the router left unquantized).
+#
+# Reading of "per-channel" (the recipe does not spell it out): one fp32 scale
+# per output row of each expert matrix, s = max|row| / 448 (448 is the largest
+# finite E4M3FN value), q = E4M3FN(w / s) by round-to-nearest-even, the
+# quotient clamped to +-448 first (fp32 rounding of s can push the row maximum
+# a hair past 448); a row of zeros gets s = 1.  The GEMM uses s * q.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def _e4m3_table():
+    """fp64 value of every E4M3FN bit pattern (OCP FP8: bias 7, 3 mantissa
+    bits, S.1111.111 is NaN, no infinities), from the format definition."""
+    vals = np.empty(256)
+    for b in range(256):
+        sgn = -1.0 if b & 0x80 else 1.0
+        e, m = (b >> 3) & 0xF, b & 0x7
+        if e == 0xF and m == 0x7:
+            vals[b] = np.nan
+        elif e == 0:
+            vals[b] = sgn * m * 2.0 ** -9
+        else:
+            vals[b] = sgn * (1 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3 = _e4m3_table()
+
+
+def e4m3_decode(q):
+    """fp64 values of E4M3FN codes (uint8 array)."""
+    return _E4M3[np.asarray(q, dtype=np.uint8)]
+
+
+def e4m3_encode(x):
+    """Round fp32 values (|x| <= 448) to the nearest E4M3FN code, ties to the
+    code with an even mantissa (round-to-nearest-even), by search over the
+    finite codes of the same sign."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if np.any(np.abs(x) > E4M3_MAX) or np.any(~np.isfinite(x)):
+        raise ValueError("e4m3_encode: value outside the finite E4M3FN range")
+    pos = np.array([b for b in range(0x7F)])          # 0x00 .. 0x7E: +0 .. +448
+    pv = _E4M3[pos]
+    a = np.abs(x).ravel()
+    idx = np.searchsorted(pv, a)                      # pv[idx-1] < a <= pv[idx]
+    idx = np.clip(idx, 1, len(pv) - 1)
+    lo, hi = pv[idx - 1], pv[idx]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & ((pos[idx] & 1) == 0))
+    code = np.where(a <= lo, pos[idx - 1], np.where(pick_hi, pos[idx], pos[idx - 1]))
+    code = np.where(a == 0, 0, code)
+    sign = (x.ravel() < 0) | ((x.ravel() == 0) & np.signbit(x.ravel()))
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8).reshape(x.shape)
+
+
+def quantize_fp8_per_channel(w):
+    """(codes uint8 [..., N, K], scales fp32 [..., N]) of a row-major weight
+    [..., N, K]: s = fp32(max|row| / 448), q = E4M3FN(clamp(fp32(w / s), +-448))."""
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=-1)
+    s = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0))
+    s = s.astype(np.float32)
+    ratio = (w32 / s[..., None]).astype(np.float32)
+    ratio = np.clip(ratio, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_encode(ratio), s
+
+
+def dequantize_fp8(q, s):
+    """fp64 weights s * decode(q)."""
+    return e4m3_decode(q) * np.asarray(s, dtype=np.float64)[..., None]
