@@ -11,7 +11,8 @@ include/beam_moe.h); this package only marshals torch tensors into it.
 """
 from ._lib import (  # noqa: F401
     ENTRY_EXPERT_FFN, ENTRY_EXPERT_STAGE, ENTRY_LAYER, ENTRY_PERMUTE, ENTRY_ROUTE, EXPORTS,
-    LAYOUT_PACKED, LAYOUT_ROW_MAJOR, LIB_PATH, MoeConfig, MoeError, Workspace, combine,
-    expert_down, expert_ffn, expert_gate_up, layer_forward, lib, make_config, pack_weights,
-    permute, route, route_replay, status_string, workspace_bytes,
+    LAYOUT_FP8_PACKED, LAYOUT_PACKED, LAYOUT_ROW_MAJOR, LIB_PATH, Fp8Weights, MoeConfig,
+    MoeError, Workspace, combine, expert_down, expert_down_fp8, expert_ffn, expert_ffn_fp8,
+    expert_gate_up, expert_gate_up_fp8, layer_forward, layer_forward_fp8, lib, make_config,
+    pack_weights, permute, quantize_fp8, route, route_replay, status_string, workspace_bytes,
 )

@@ -29,11 +29,14 @@ ENTRY_EXPERT_STAGE = 4
 
 LAYOUT_ROW_MAJOR = 0
 LAYOUT_PACKED = 1
+LAYOUT_FP8_PACKED = 2
 
 #: Every symbol include/beam_moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_replay", "moe_permute",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_layer_forward", "moe_pack_weights", "moe_status_string")
+           "moe_layer_forward", "moe_pack_weights", "moe_quantize_fp8", "moe_expert_ffn_fp8",
+           "moe_expert_gate_up_fp8", "moe_expert_down_fp8", "moe_layer_forward_fp8",
+           "moe_status_string")
 
 
 class MoeConfig(ctypes.Structure):
@@ -80,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [CP, P, P, P, P, P]
         L.moe_pack_weights.argtypes = [CP, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
+        L.moe_quantize_fp8.argtypes = [CP, P, P, P, P, P, P, P]
+        L.moe_expert_ffn_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
+        L.moe_expert_gate_up_fp8.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
+        L.moe_expert_down_fp8.argtypes = [CP, P, P, P, P, P, P, Z, P]
+        L.moe_layer_forward_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         L.moe_status_string.argtypes = [I]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -349,3 +357,139 @@ def pack_weights(w_gate_up=None, w_down=None):
                                                      _ptr(w_down), _ptr(pgu), _ptr(pd),
                                                      _stream(ref.device)))
     return pgu, pd
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3FN) per-channel expert weights
+class Fp8Weights:
+    """Quantised expert weights: codes uint8 in the fp8 fragment layout
+    (q_gate_up [E, 2I, H], q_down [E, H, I]) and fp32 per-row scales
+    (s_gate_up [E, 2I], s_down [E, H])."""
+
+    def __init__(self, q_gate_up, s_gate_up, q_down, s_down):
+        self.q_gate_up, self.s_gate_up = q_gate_up, s_gate_up
+        self.q_down, self.s_down = q_down, s_down
+
+    @property
+    def shape(self):
+        """(E, H, I)."""
+        E, I2, H = self.q_gate_up.shape
+        return E, H, I2 // 2
+
+    def check(self, device):
+        E, H, I = self.shape
+        _check(self.q_gate_up, "q_gate_up", torch.uint8, (E, 2 * I, H), device)
+        _check(self.s_gate_up, "s_gate_up", torch.float32, (E, 2 * I), device)
+        _check(self.q_down, "q_down", torch.uint8, (E, H, I), device)
+        _check(self.s_down, "s_down", torch.float32, (E, H), device)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.q_gate_up, self.s_gate_up, self.q_down, self.s_down))
+
+
+def quantize_fp8(w_gate_up, w_down) -> Fp8Weights:
+    """Per-channel FP8 quantisation of row-major bf16 expert weights."""
+    E, I2, H = w_gate_up.shape
+    I = I2 // 2
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H))
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), w_gate_up.device)
+    dev = w_gate_up.device
+    cfg = make_config(0, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=1)
+    f = Fp8Weights(torch.empty(E, 2 * I, H, dtype=torch.uint8, device=dev),
+                   torch.empty(E, 2 * I, dtype=torch.float32, device=dev),
+                   torch.empty(E, H, I, dtype=torch.uint8, device=dev),
+                   torch.empty(E, H, dtype=torch.float32, device=dev))
+    _call("moe_quantize_fp8", lib().moe_quantize_fp8(
+        ctypes.byref(cfg), _ptr(w_gate_up), _ptr(w_down), _ptr(f.q_gate_up), _ptr(f.s_gate_up),
+        _ptr(f.q_down), _ptr(f.s_down), _stream(dev)))
+    return f
+
+
+def expert_ffn_fp8(x, perm_src, offsets, w: Fp8Weights, *, topk=8, workspace=None):
+    """expert_ffn with FP8 weights: y_perm bf16 [T*k, H]."""
+    T, H = x.shape
+    E, _, I = w.shape
+    _check(x, "x", torch.bfloat16, (T, H))
+    w.check(x.device)
+    _check(perm_src, "perm_src", torch.int32, (T * topk,), x.device)
+    _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=LAYOUT_FP8_PACKED)
+    y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_FFN)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_expert_ffn_fp8", lib().moe_expert_ffn_fp8(
+        ctypes.byref(cfg), _ptr(x), _ptr(perm_src), _ptr(offsets), _ptr(w.q_gate_up),
+        _ptr(w.s_gate_up), _ptr(w.q_down), _ptr(w.s_down), _ptr(y), _ptr(ws), nb,
+        _stream(x.device)))
+    return y
+
+
+def expert_gate_up_fp8(x, perm_src, offsets, w: Fp8Weights, *, topk=8, workspace=None):
+    """expert_gate_up with FP8 weights: h bf16 [T*k, I]."""
+    T, H = x.shape
+    E, _, I = w.shape
+    _check(x, "x", torch.bfloat16, (T, H))
+    w.check(x.device)
+    _check(perm_src, "perm_src", torch.int32, (T * topk,), x.device)
+    _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=LAYOUT_FP8_PACKED)
+    h = torch.empty(T * topk, I, dtype=torch.bfloat16, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_STAGE)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_expert_gate_up_fp8", lib().moe_expert_gate_up_fp8(
+        ctypes.byref(cfg), _ptr(x), _ptr(perm_src), _ptr(offsets), _ptr(w.q_gate_up),
+        _ptr(w.s_gate_up), _ptr(h), _ptr(ws), nb, _stream(x.device)))
+    return h
+
+
+def expert_down_fp8(h, offsets, w: Fp8Weights, *, topk=8, workspace=None):
+    """expert_down with FP8 weights: y_perm bf16 [T*k, H]."""
+    R, I = h.shape
+    E, H, _ = w.shape
+    T = R // topk
+    _check(h, "h", torch.bfloat16, (T * topk, I))
+    w.check(h.device)
+    _check(offsets, "offsets", torch.int32, (E + 1,), h.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=LAYOUT_FP8_PACKED)
+    y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=h.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_STAGE)
+    ws = _ws(workspace, h.device).get(nb, h.device)
+    _call("moe_expert_down_fp8", lib().moe_expert_down_fp8(
+        ctypes.byref(cfg), _ptr(h), _ptr(offsets), _ptr(w.q_down), _ptr(w.s_down), _ptr(y),
+        _ptr(ws), nb, _stream(h.device)))
+    return y
+
+
+def layer_forward_fp8(x, w_router, w: Fp8Weights, *, sel_bias=None, num_groups=8, topk_groups=4,
+                      topk=8, renormalize=True, routed_scaling=2.5, return_routing=False,
+                      out=None, workspace=None):
+    """layer_forward with FP8 expert weights."""
+    T, H = x.shape
+    E, _, I = w.shape
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(w_router, "w_router", torch.float32, (E, H), x.device)
+    w.check(x.device)
+    if sel_bias is not None:
+        _check(sel_bias, "sel_bias", torch.float32, (E,), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=num_groups, topk_groups=topk_groups,
+                      topk=topk, renormalize=renormalize, routed_scaling=routed_scaling,
+                      weight_layout=LAYOUT_FP8_PACKED)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    else:
+        _check(out, "out", torch.bfloat16, (T, H), x.device)
+    ids = tw = None
+    if return_routing:
+        ids = torch.empty(T, topk, dtype=torch.int32, device=x.device)
+        tw = torch.empty(T, topk, dtype=torch.float32, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_LAYER)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    _call("moe_layer_forward_fp8", lib().moe_layer_forward_fp8(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(w.q_gate_up),
+        _ptr(w.s_gate_up), _ptr(w.q_down), _ptr(w.s_down), _ptr(out), _ptr(ids), _ptr(tw),
+        _ptr(ws), nb, _stream(x.device)))
+    return (out, ids, tw) if return_routing else out

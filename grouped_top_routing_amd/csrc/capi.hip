@@ -19,7 +19,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int validate(const moe_config_t* c) {
+// Weight layouts an entry point accepts (bit i = layout i).
+constexpr int kBf16Layouts = (1 << MOE_LAYOUT_ROW_MAJOR) | (1 << MOE_LAYOUT_PACKED);
+constexpr int kFp8Layouts = 1 << MOE_LAYOUT_FP8_PACKED;
+constexpr int kAnyLayout = kBf16Layouts | kFp8Layouts;
+
+int validate(const moe_config_t* c, int layouts = kBf16Layouts) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->num_tokens < 0 || c->hidden <= 0 || c->intermediate <= 0 || c->num_experts <= 0 ||
       c->num_groups <= 0 || c->topk_groups <= 0 || c->topk <= 0)
@@ -27,7 +32,7 @@ int validate(const moe_config_t* c) {
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->routed_scaling)) return MOE_ERR_INVALID_ARG;
   if (c->num_experts % c->num_groups != 0) return MOE_ERR_INVALID_ARG;
-  if (c->weight_layout != MOE_LAYOUT_ROW_MAJOR && c->weight_layout != MOE_LAYOUT_PACKED)
+  if (c->weight_layout < 0 || c->weight_layout > 2 || !((layouts >> c->weight_layout) & 1))
     return MOE_ERR_INVALID_ARG;
   if (c->topk_groups > c->num_groups) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c->topk > (int64_t)c->topk_groups * (c->num_experts / c->num_groups))
@@ -44,10 +49,15 @@ int validate(const moe_config_t* c) {
 int64_t pairs(const moe_config_t* c) { return c->num_tokens * (int64_t)c->topk; }
 
 int mb_for(const moe_config_t* c) { return ffn_choose_mb(pairs(c), c->num_experts); }
+int mb_for_fp8(const moe_config_t* c) { return ffn_fp8_choose_mb(pairs(c), c->num_experts); }
 
+// Upper bound on the m-tiles of either weight format's plan (one workspace
+// size serves the bf16 and the fp8 entry points).
 int64_t max_tiles_for(const moe_config_t* c) {
   const int64_t n = pairs(c);
-  const int64_t bmax = ffn_rows_per_tile(mb_for(c));
+  int64_t bmax = ffn_rows_per_tile(mb_for(c));
+  const int64_t b8 = ffn_rows_per_tile(mb_for_fp8(c));
+  if (b8 < bmax) bmax = b8;
   return n / bmax + (n < c->num_experts ? n : c->num_experts) + 1;
 }
 
@@ -122,8 +132,8 @@ int do_permute(const moe_config_t* c, const int32_t* ids, int32_t* counts, int32
                                    static_cast<int32_t*>(scratch), s));
 }
 
-int do_plan(const moe_config_t* c, const int32_t* offsets, int32_t* plan, hipStream_t s) {
-  return hip_status(launch_tile_plan(offsets, c->num_experts, ffn_rows_per_tile(mb_for(c)), plan,
+int do_plan(const moe_config_t* c, const int32_t* offsets, int32_t* plan, int mb, hipStream_t s) {
+  return hip_status(launch_tile_plan(offsets, c->num_experts, ffn_rows_per_tile(mb), plan,
                                      (int)max_tiles_for(c), s));
 }
 
@@ -151,10 +161,89 @@ int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const 
            const uint16_t* wgu, const uint16_t* wd, uint16_t* y, void* scratch, hipStream_t s) {
   int32_t* plan = static_cast<int32_t*>(scratch);
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + plan_bytes(c));
-  int st = do_plan(c, offsets, plan, s);
+  int st = do_plan(c, offsets, plan, mb_for(c), s);
   if (st) return st;
   if ((st = do_gate_up(c, x, psrc, plan, wgu, h, s))) return st;
   return do_down(c, h, plan, wd, y, s);
+}
+
+// ---- fp8 expert weights ----
+struct Fp8Weights {
+  const uint8_t* q_gate_up;
+  const float* s_gate_up;
+  const uint8_t* q_down;
+  const float* s_down;
+};
+
+int do_gate_up_fp8(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
+                   const int32_t* plan, const uint8_t* q, const float* sc, uint16_t* h,
+                   hipStream_t s) {
+  const int64_t max_tiles = max_tiles_for(c);
+  const int H = c->hidden, I = c->intermediate;
+  return hip_status(launch_grouped_gemm_fp8(mb_for_fp8(c), true, x, psrc, c->topk, q, sc,
+                                            (int64_t)2 * I * H, 2 * I, h, plan, (int)max_tiles, H,
+                                            I, I, max_tiles * (I / ffn_out_cols_per_item(true)),
+                                            s));
+}
+
+int do_down_fp8(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint8_t* q,
+                const float* sc, uint16_t* y, hipStream_t s) {
+  const int64_t max_tiles = max_tiles_for(c);
+  const int H = c->hidden, I = c->intermediate;
+  return hip_status(launch_grouped_gemm_fp8(mb_for_fp8(c), false, h, nullptr, c->topk, q, sc,
+                                            (int64_t)H * I, H, y, plan, (int)max_tiles, I, H, 0,
+                                            max_tiles * (H / ffn_out_cols_per_item(false)), s));
+}
+
+int do_ffn_fp8(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
+               const int32_t* offsets, const Fp8Weights& w, uint16_t* y, void* scratch,
+               hipStream_t s) {
+  int32_t* plan = static_cast<int32_t*>(scratch);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + plan_bytes(c));
+  int st = do_plan(c, offsets, plan, mb_for_fp8(c), s);
+  if (st) return st;
+  if ((st = do_gate_up_fp8(c, x, psrc, plan, w.q_gate_up, w.s_gate_up, h, s))) return st;
+  return do_down_fp8(c, h, plan, w.q_down, w.s_down, y, s);
+}
+
+bool fp8_weights_ok(const uint8_t* q, const float* sc) {
+  return q && sc && aligned16(q) && aligned4(sc);
+}
+
+// The whole block around an expert-MLP step `ffn(x, psrc, offsets, y, scratch)`.
+template <class Ffn>
+int layer_common(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                 const float* sel_bias, uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
+                 void* workspace, size_t workspace_bytes, hipStream_t s, Ffn ffn) {
+  const LayerLayout L = layer_layout(cfg);
+  int st = check_ws(workspace, workspace_bytes, L.total);
+  if (st) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* psrc = reinterpret_cast<int32_t*>(ws + L.psrc);
+  int32_t* pdst = reinterpret_cast<int32_t*>(ws + L.pdst);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+  void* scratch = ws + L.scratch;
+  if ((st = do_route(cfg, x, w_router, sel_bias, ids, w, scratch, s))) return st;
+  if ((st = do_permute(cfg, ids, counts, offsets, psrc, pdst, scratch, s))) return st;
+  if ((st = ffn(psrc, offsets, y, scratch))) return st;
+  return hip_status(launch_combine(y, pdst, w, out, (int)cfg->num_tokens, cfg->hidden, cfg->topk,
+                                   cfg->routed_scaling, s));
+}
+
+bool layer_args_ok(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                   const float* sel_bias, uint16_t* out, int32_t* topk_ids_out,
+                   float* topk_w_out) {
+  (void)cfg;
+  if (!x || !w_router || !out) return false;
+  return aligned16(x) && aligned16(w_router) && aligned16(out) &&
+         (!sel_bias || aligned4(sel_bias)) && (!topk_ids_out || aligned4(topk_ids_out)) &&
+         (!topk_w_out || aligned4(topk_w_out));
 }
 
 }  // namespace
@@ -173,7 +262,7 @@ const char* moe_status_string(int status) {
 }
 
 int moe_workspace_bytes(const moe_config_t* cfg, int entry, size_t* bytes) {
-  int st = validate(cfg);
+  int st = validate(cfg, kAnyLayout);
   if (st) return st;
   if (!bytes) return MOE_ERR_INVALID_ARG;
   switch (entry) {
@@ -190,7 +279,7 @@ int moe_workspace_bytes(const moe_config_t* cfg, int entry, size_t* bytes) {
 int moe_route(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
               const float* sel_bias, int32_t* topk_ids, float* topk_w, void* workspace,
               size_t workspace_bytes, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, kAnyLayout);
   if (st) return st;
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w) ||
@@ -206,7 +295,7 @@ int moe_route(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
 int moe_route_replay(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
                      const int32_t* topk_ids, float* topk_w, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, kAnyLayout);
   if (st) return st;
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w))
@@ -227,7 +316,7 @@ int moe_route_replay(const moe_config_t* cfg, const uint16_t* x, const float* w_
 int moe_permute(const moe_config_t* cfg, const int32_t* topk_ids, int32_t* counts,
                 int32_t* offsets, int32_t* perm_src, int32_t* perm_dst, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, kAnyLayout);
   if (st) return st;
   if (!topk_ids || !counts || !offsets || !perm_src || !perm_dst) return MOE_ERR_INVALID_ARG;
   if (!aligned4(topk_ids) || !aligned4(counts) || !aligned4(offsets) || !aligned4(perm_src) ||
@@ -270,7 +359,7 @@ int moe_expert_gate_up(const moe_config_t* cfg, const uint16_t* x, const int32_t
   if ((st = device_ready())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* plan = static_cast<int32_t*>(workspace);
-  if ((st = do_plan(cfg, offsets, plan, s))) return st;
+  if ((st = do_plan(cfg, offsets, plan, mb_for(cfg), s))) return st;
   return do_gate_up(cfg, x, perm_src, plan, w_gate_up, h, s);
 }
 
@@ -287,7 +376,7 @@ int moe_expert_down(const moe_config_t* cfg, const uint16_t* h, const int32_t* o
   if ((st = device_ready())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* plan = static_cast<int32_t*>(workspace);
-  if ((st = do_plan(cfg, offsets, plan, s))) return st;
+  if ((st = do_plan(cfg, offsets, plan, mb_for(cfg), s))) return st;
   return do_down(cfg, h, plan, w_down, y_perm, s);
 }
 
@@ -295,6 +384,7 @@ int moe_pack_weights(const moe_config_t* cfg, const uint16_t* w_gate_up, const u
                      uint16_t* packed_gate_up, uint16_t* packed_down, void* stream) {
   moe_config_t c = cfg ? *cfg : moe_config_t{};
   c.num_tokens = 0;
+  c.weight_layout = MOE_LAYOUT_ROW_MAJOR;  // not read here
   int st = validate(cfg ? &c : nullptr);
   if (st) return st;
   if ((w_gate_up == nullptr) != (packed_gate_up == nullptr) ||
@@ -324,7 +414,7 @@ int moe_pack_weights(const moe_config_t* cfg, const uint16_t* w_gate_up, const u
 
 int moe_combine(const moe_config_t* cfg, const uint16_t* y_perm, const int32_t* perm_dst,
                 const float* topk_w, uint16_t* out, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, kAnyLayout);
   if (st) return st;
   if (!y_perm || !perm_dst || !topk_w || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_perm) || !aligned16(out) || !aligned4(perm_dst) || !aligned4(topk_w))
@@ -342,30 +432,127 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
                       size_t workspace_bytes, void* stream) {
   int st = validate(cfg);
   if (st) return st;
-  if (!x || !w_router || !w_gate_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate_up) || !aligned16(w_down) ||
-      !aligned16(out) || (sel_bias && !aligned4(sel_bias)) ||
-      (topk_ids_out && !aligned4(topk_ids_out)) || (topk_w_out && !aligned4(topk_w_out)))
+  if (!layer_args_ok(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out) || !w_gate_up ||
+      !w_down || !aligned16(w_gate_up) || !aligned16(w_down))
     return MOE_ERR_INVALID_ARG;
-  const LayerLayout L = layer_layout(cfg);
-  if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return layer_common(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out, workspace,
+                      workspace_bytes, s,
+                      [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* scratch) {
+                        return do_ffn(cfg, x, psrc, offsets, w_gate_up, w_down, y, scratch, s);
+                      });
+}
+
+int moe_quantize_fp8(const moe_config_t* cfg, const uint16_t* w_gate_up, const uint16_t* w_down,
+                     uint8_t* q_gate_up, float* s_gate_up, uint8_t* q_down, float* s_down,
+                     void* stream) {
+  moe_config_t c = cfg ? *cfg : moe_config_t{};
+  c.num_tokens = 0;
+  c.weight_layout = MOE_LAYOUT_ROW_MAJOR;  // not read here
+  int st = validate(cfg ? &c : nullptr);
+  if (st) return st;
+  const bool gu = w_gate_up || q_gate_up || s_gate_up;
+  const bool dn = w_down || q_down || s_down;
+  if (gu && (!w_gate_up || !q_gate_up || !s_gate_up)) return MOE_ERR_INVALID_ARG;
+  if (dn && (!w_down || !q_down || !s_down)) return MOE_ERR_INVALID_ARG;
+  if ((gu && (!aligned16(w_gate_up) || !aligned16(q_gate_up) || !aligned4(s_gate_up))) ||
+      (dn && (!aligned16(w_down) || !aligned16(q_down) || !aligned4(s_down))))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t E = c.num_experts, H = c.hidden, I = c.intermediate;
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+  };
+  const int64_t ngu = E * 2 * I * H, ndn = E * H * I;
+  if (gu && (overlap(w_gate_up, 2 * ngu, q_gate_up, ngu) ||
+             overlap(w_gate_up, 2 * ngu, s_gate_up, 4 * E * 2 * I) ||
+             overlap(q_gate_up, ngu, s_gate_up, 4 * E * 2 * I)))
+    return MOE_ERR_INVALID_ARG;
+  if (dn && (overlap(w_down, 2 * ndn, q_down, ndn) || overlap(w_down, 2 * ndn, s_down, 4 * E * H) ||
+             overlap(q_down, ndn, s_down, 4 * E * H)))
+    return MOE_ERR_INVALID_ARG;
+  if (!gu && !dn) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (gu && (st = hip_status(launch_quantize_fp8(w_gate_up, q_gate_up, s_gate_up, (int)E,
+                                                 (int)(2 * I), (int)H, s))))
+    return st;
+  if (dn && (st = hip_status(launch_quantize_fp8(w_down, q_down, s_down, (int)E, (int)H, (int)I, s))))
+    return st;
+  return MOE_OK;
+}
+
+int moe_expert_ffn_fp8(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                       const int32_t* offsets, const uint8_t* q_gate_up, const float* s_gate_up,
+                       const uint8_t* q_down, const float* s_down, uint16_t* y_perm,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(cfg, kFp8Layouts);
+  if (st) return st;
+  if (!x || !perm_src || !offsets || !y_perm || !fp8_weights_ok(q_gate_up, s_gate_up) ||
+      !fp8_weights_ok(q_down, s_down))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y_perm) || !aligned4(perm_src) || !aligned4(offsets))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, ffn_ws(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  return do_ffn_fp8(cfg, x, perm_src, offsets, Fp8Weights{q_gate_up, s_gate_up, q_down, s_down},
+                    y_perm, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_gate_up_fp8(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                           const int32_t* offsets, const uint8_t* q_gate_up,
+                           const float* s_gate_up, uint16_t* h, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int st = validate(cfg, kFp8Layouts);
+  if (st) return st;
+  if (!x || !perm_src || !offsets || !h || !fp8_weights_ok(q_gate_up, s_gate_up))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(h) || !aligned4(perm_src) || !aligned4(offsets))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, plan_bytes(cfg)))) return st;
   if (cfg->num_tokens == 0) return MOE_OK;
   if ((st = device_ready())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
-  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  int32_t* psrc = reinterpret_cast<int32_t*>(ws + L.psrc);
-  int32_t* pdst = reinterpret_cast<int32_t*>(ws + L.pdst);
-  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
-  void* scratch = ws + L.scratch;
-  if ((st = do_route(cfg, x, w_router, sel_bias, ids, w, scratch, s))) return st;
-  if ((st = do_permute(cfg, ids, counts, offsets, psrc, pdst, scratch, s))) return st;
-  if ((st = do_ffn(cfg, x, psrc, offsets, w_gate_up, w_down, y, scratch, s))) return st;
-  return hip_status(launch_combine(y, pdst, w, out, (int)cfg->num_tokens, cfg->hidden, cfg->topk,
-                                   cfg->routed_scaling, s));
+  int32_t* plan = static_cast<int32_t*>(workspace);
+  if ((st = do_plan(cfg, offsets, plan, mb_for_fp8(cfg), s))) return st;
+  return do_gate_up_fp8(cfg, x, perm_src, plan, q_gate_up, s_gate_up, h, s);
+}
+
+int moe_expert_down_fp8(const moe_config_t* cfg, const uint16_t* h, const int32_t* offsets,
+                        const uint8_t* q_down, const float* s_down, uint16_t* y_perm,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(cfg, kFp8Layouts);
+  if (st) return st;
+  if (!h || !offsets || !y_perm || !fp8_weights_ok(q_down, s_down)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(y_perm) || !aligned4(offsets)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, plan_bytes(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* plan = static_cast<int32_t*>(workspace);
+  if ((st = do_plan(cfg, offsets, plan, mb_for_fp8(cfg), s))) return st;
+  return do_down_fp8(cfg, h, plan, q_down, s_down, y_perm, s);
+}
+
+int moe_layer_forward_fp8(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                          const float* sel_bias, const uint8_t* q_gate_up, const float* s_gate_up,
+                          const uint8_t* q_down, const float* s_down, uint16_t* out,
+                          int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = validate(cfg, kFp8Layouts);
+  if (st) return st;
+  if (!layer_args_ok(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out) ||
+      !fp8_weights_ok(q_gate_up, s_gate_up) || !fp8_weights_ok(q_down, s_down))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Fp8Weights w{q_gate_up, s_gate_up, q_down, s_down};
+  return layer_common(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out, workspace,
+                      workspace_bytes, s,
+                      [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* scratch) {
+                        return do_ffn_fp8(cfg, x, psrc, offsets, w, y, scratch, s);
+                      });
 }
 
 }  // extern "C"

@@ -33,6 +33,14 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
 hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N, int K,
                                hipStream_t stream);
 
+int ffn_fp8_choose_mb(int64_t rows, int E);
+hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
+                                   int topk, const uint8_t* Q, const float* scales, int64_t qstride,
+                                   int N, uint16_t* C, const int32_t* plan, int max_tiles, int K,
+                                   int n_out, int up_row0, int64_t max_items, hipStream_t stream);
+hipError_t launch_quantize_fp8(const uint16_t* w, uint8_t* q, float* scales, int E, int N, int K,
+                               hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
                           uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream);
 

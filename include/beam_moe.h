@@ -77,16 +77,21 @@ typedef struct moe_config {
                              scores ("normalized router weights"); 0: raw score   */
   float routed_scaling;   /* factor applied to the combined output, 2.5          */
   int32_t weight_layout;  /* expert weight storage: MOE_LAYOUT_ROW_MAJOR or
-                             MOE_LAYOUT_PACKED (written by moe_pack_weights)     */
+                             MOE_LAYOUT_PACKED (written by moe_pack_weights) for
+                             the bf16 expert calls, MOE_LAYOUT_FP8_PACKED for the
+                             *_fp8 calls; calls that read no expert weights
+                             accept any of the three                              */
 } moe_config_t;
 
 /* Expert weight layouts. */
 enum moe_weight_layout {
   MOE_LAYOUT_ROW_MAJOR = 0,  /* w_gate_up [E, 2I, H], w_down [E, H, I], row-major    */
-  MOE_LAYOUT_PACKED = 1      /* same sizes, each expert's [N, K] matrix stored as
+  MOE_LAYOUT_PACKED = 1,     /* same sizes, each expert's [N, K] matrix stored as
                                 [N/16][K/32][64][8]: the 16 x 32 bf16 operand tiles of
                                 the gfx950 matrix cores, lane-ordered, consecutive
                                 along K (see moe_pack_weights)                        */
+  MOE_LAYOUT_FP8_PACKED = 2  /* E4M3FN codes plus fp32 per-row scales (see
+                                moe_quantize_fp8)                                     */
 };
 
 /* Bytes of workspace `entry` needs for `cfg` (written to *bytes). */
@@ -189,10 +194,65 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
  *   w_gate_up, w_down            row-major inputs (shapes as above)
  *   packed_gate_up, packed_down  outputs of the same sizes; must not overlap
  *                                the inputs
- * Either pair may be NULL to skip it.  num_tokens is ignored.
+ * Either pair may be NULL to skip it.  num_tokens and weight_layout are
+ * ignored.
  */
 int moe_pack_weights(const moe_config_t* cfg, const uint16_t* w_gate_up, const uint16_t* w_down,
                      uint16_t* packed_gate_up, uint16_t* packed_down, void* stream);
+
+/*
+ * FP8 per-channel expert weights (vLLM recipe JSON "Beam-1.0-501B-A23B",
+ * precision variant fp8: FP8 per-channel weights, router unquantized).
+ *
+ * Each expert matrix row n (output channel) has one fp32 scale s[n] and
+ * E4M3FN codes q[n, k] (OCP FP8: 1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, largest finite value 448); the matrix the GEMMs use is
+ * w[n, k] = s[n] * q[n, k].  Activations stay bf16, accumulation fp32, and
+ * the scale multiplies the fp32 accumulator of its output column.  The
+ * router, selection, permutation and combine are the bf16 path's.
+ *
+ * Code layout (MOE_LAYOUT_FP8_PACKED): each expert's [N, K] code matrix is
+ * stored as [N/16][K/64][64][16] bytes; entry (b, s, l) holds row
+ * 16b + l%16, bytes 0..7 at k = 64s + 8(l/16) .. +7 and bytes 8..15 at
+ * k = 64s + 32 + 8(l/16) .. +7.  Scales are plain fp32 [E, N].
+ *   q_gate_up [E, 2*I, H] codes, s_gate_up [E, 2*I]
+ *   q_down    [E, H, I]   codes, s_down    [E, H]
+ * The *_fp8 calls require cfg->weight_layout == MOE_LAYOUT_FP8_PACKED (else
+ * MOE_ERR_INVALID_ARG).  Their workspace sizes are the ones moe_workspace_bytes
+ * gives for MOE_ENTRY_EXPERT_FFN, MOE_ENTRY_EXPERT_STAGE and MOE_ENTRY_LAYER.
+ */
+/*
+ * Quantise row-major bf16 expert weights: s[n] = fp32(max_k |w[n, k]|) / 448
+ * in fp32 (1 for an all-zero row); q[n, k] = E4M3FN(clamp(w[n, k] / s[n],
+ * -448, 448)) with fp32 division and round-to-nearest-even (ties to the even
+ * code); codes are written in MOE_LAYOUT_FP8_PACKED.
+ *   w_gate_up, w_down  row-major bf16 inputs [E, 2I, H], [E, H, I]
+ *   q_*, s_*           outputs as above; must not overlap the inputs
+ * Either set (w, q, s) may be all NULL to skip it.  num_tokens and
+ * weight_layout are ignored.
+ */
+int moe_quantize_fp8(const moe_config_t* cfg, const uint16_t* w_gate_up, const uint16_t* w_down,
+                     uint8_t* q_gate_up, float* s_gate_up, uint8_t* q_down, float* s_down,
+                     void* stream);
+
+/* moe_expert_ffn, moe_expert_gate_up, moe_expert_down and moe_layer_forward
+ * with FP8 expert weights (arguments as in those calls). */
+int moe_expert_ffn_fp8(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                       const int32_t* offsets, const uint8_t* q_gate_up, const float* s_gate_up,
+                       const uint8_t* q_down, const float* s_down, uint16_t* y_perm,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int moe_expert_gate_up_fp8(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                           const int32_t* offsets, const uint8_t* q_gate_up,
+                           const float* s_gate_up, uint16_t* h,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int moe_expert_down_fp8(const moe_config_t* cfg, const uint16_t* h, const int32_t* offsets,
+                        const uint8_t* q_down, const float* s_down, uint16_t* y_perm,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int moe_layer_forward_fp8(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                          const float* sel_bias, const uint8_t* q_gate_up, const float* s_gate_up,
+                          const uint8_t* q_down, const float* s_down, uint16_t* out,
+                          int32_t* topk_ids_out, float* topk_w_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* moe_status_string(int status);

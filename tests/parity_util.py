@@ -89,3 +89,35 @@ def layer_reference(ids_gpu, ref, x, experts, *, renormalize=True, scale=2.5):
             acc += wt[j] * oracle.ffn_rows(np.asarray(x)[t:t + 1], *get(int(e)))[0]
         out[t] = scale * acc
     return out
+
+
+def unpack_fp8_codes(q):
+    """Row-major [E, N, K] codes from the library's fp8 fragment layout
+    ([N/16][K/64][64 lanes][16 bytes] per expert; lane l = r + 16g holds row
+    16b + r, bytes 0..7 at k = 64s + 8g + j and bytes 8..15 at
+    k = 64s + 32 + 8g + j)."""
+    q = np.asarray(q, dtype=np.uint8)
+    E, N, K = q.shape
+    p = q.reshape(E, N // 16, K // 64, 4, 16, 2, 8)        # e, b, s, g, r, h, j
+    return p.transpose(0, 1, 4, 2, 5, 3, 6).reshape(E, N, K)  # e, b, r, s, h, g, j
+
+
+class OracleFp8Experts:
+    """Expert weights as the oracle quantises them (from the bf16 weights),
+    dequantised to fp64: a callable e -> (gate_up, down), cached per expert."""
+
+    def __init__(self, w_gate_up, w_down):
+        self._gu, self._dn = w_gate_up, w_down
+        self._cache = {}
+
+    def quantized(self, e):
+        gu = np.asarray(self._gu[e] if not callable(self._gu) else self._gu(e), np.float32)
+        dn = np.asarray(self._dn[e] if not callable(self._dn) else self._dn(e), np.float32)
+        return oracle.quantize_fp8_per_channel(gu), oracle.quantize_fp8_per_channel(dn)
+
+    def __call__(self, e):
+        e = int(e)
+        if e not in self._cache:
+            (qg, sg), (qd, sd) = self.quantized(e)
+            self._cache[e] = (oracle.dequantize_fp8(qg, sg), oracle.dequantize_fp8(qd, sd))
+        return self._cache[e]

@@ -141,7 +141,7 @@ def test_python_binding_requires_device_tensors():
 
 
 def test_weight_layout_and_pack_validation():
-    cfg = _cfg(weight_layout=2)
+    cfg = _cfg(weight_layout=3)
     n = ctypes.c_size_t(0)
     lib = gtr.lib()
     assert lib.moe_workspace_bytes(ctypes.byref(cfg), L.ENTRY_LAYER, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
@@ -156,3 +156,64 @@ def test_weight_layout_and_pack_validation():
                                 None) == L.MOE_ERR_INVALID_ARG
     # nothing to do
     assert lib.moe_pack_weights(ctypes.byref(cfg), None, None, None, None, None) == L.MOE_OK
+
+
+def _fp8_cfg(**kw):
+    kw.setdefault("weight_layout", L.LAYOUT_FP8_PACKED)
+    return _cfg(**kw)
+
+
+def test_fp8_entry_points_validate_layout_pointers_and_workspace():
+    lib = gtr.lib()
+    cfg = _fp8_cfg()
+    big = 1 << 40
+    ffn = lambda c, **p: lib.moe_expert_ffn_fp8(
+        ctypes.byref(c), p.get("x", A), A, A, p.get("qgu", A), p.get("sgu", A), p.get("qd", A),
+        p.get("sd", A), A, p.get("ws", A), p.get("nb", big), None)
+    # the fp8 calls need the fp8 layout, the bf16 calls refuse it
+    assert ffn(_cfg()) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), A, A, A, A, A, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    assert ffn(cfg, qgu=None) == L.MOE_ERR_INVALID_ARG
+    assert ffn(cfg, sd=None) == L.MOE_ERR_INVALID_ARG
+    assert ffn(cfg, qd=MIS) == L.MOE_ERR_INVALID_ARG
+    assert ffn(cfg, sgu=ctypes.c_void_p(0x10002)) == L.MOE_ERR_INVALID_ARG   # scales need 4 B
+    assert ffn(cfg, sgu=MIS) != L.MOE_ERR_INVALID_ARG                         # 4 B is enough
+    need = gtr.workspace_bytes(cfg, L.ENTRY_EXPERT_FFN)
+    assert ffn(cfg, nb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert gtr.workspace_bytes(cfg, L.ENTRY_EXPERT_FFN) == gtr.workspace_bytes(_cfg(), L.ENTRY_EXPERT_FFN)
+    assert lib.moe_expert_gate_up_fp8(ctypes.byref(cfg), A, A, A, None, A, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down_fp8(ctypes.byref(cfg), A, A, A, None, A, A, big, None) == L.MOE_ERR_INVALID_ARG
+    layer = lambda c, **p: lib.moe_layer_forward_fp8(
+        ctypes.byref(c), A, A, None, A, A, p.get("qd", A), A, A, None, None, A,
+        p.get("nb", big), None)
+    assert layer(cfg, qd=None) == L.MOE_ERR_INVALID_ARG
+    assert layer(cfg, nb=gtr.workspace_bytes(cfg, L.ENTRY_LAYER) - 1) == L.MOE_ERR_WORKSPACE
+    zero = _fp8_cfg(num_tokens=0)
+    assert layer(zero, nb=gtr.workspace_bytes(zero, L.ENTRY_LAYER)) == L.MOE_OK
+    # calls that read no expert weights take any layout
+    assert lib.moe_combine(ctypes.byref(_fp8_cfg(num_tokens=0)), A, A, A, A, None) == L.MOE_OK
+
+
+def test_fp8_quantize_validation():
+    lib = gtr.lib()
+    cfg = _fp8_cfg()
+    B, C = ctypes.c_void_p(0x100000000), ctypes.c_void_p(0x200000000)
+    q = lambda *p: lib.moe_quantize_fp8(ctypes.byref(cfg), *p, None)
+    assert q(None, None, None, None, None, None) == L.MOE_OK           # nothing to do
+    assert q(A, None, B, None, None, None) == L.MOE_ERR_INVALID_ARG    # scales missing
+    assert q(MIS, None, B, C, None, None) == L.MOE_ERR_INVALID_ARG     # misaligned weights
+    assert q(A, None, ctypes.c_void_p(0x10000 + 4096), C, None, None) == L.MOE_ERR_INVALID_ARG
+    assert q(A, None, B, ctypes.c_void_p(0x100000000 + 64), None, None) == L.MOE_ERR_INVALID_ARG
+    if not __import__("torch").cuda.is_available():
+        assert q(A, None, B, C, None, None) == L.MOE_ERR_HIP            # valid, no device
+
+
+def test_fp8_binding_checks_dtypes():
+    import torch
+    w = gtr.Fp8Weights(torch.zeros(256, 256, 256, dtype=torch.uint8),
+                       torch.zeros(256, 256), torch.zeros(256, 256, 128, dtype=torch.uint8),
+                       torch.zeros(256, 256))
+    assert w.shape == (256, 256, 128)
+    with pytest.raises((ValueError, TypeError)):
+        gtr.expert_ffn_fp8(torch.zeros(4, 256, dtype=torch.bfloat16),
+                           torch.zeros(32, dtype=torch.int32), torch.zeros(257, dtype=torch.int32), w)
