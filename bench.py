@@ -11,7 +11,9 @@ Prints ONE JSON line.  `value` is tokens/s of the prefill chunk (T=4096,
 hidden 5120, intermediate 2560, 256 experts); `roofline` describes the
 dominant kernel (the gate/up grouped GEMM), timed with HIP events on the
 stream it runs on; `decode` reports the weight-streaming T=32 batch in GB/s;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`fp8` times the same layer with FP8 per-channel expert weights (prefill and
+decode); `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight variant")
     p.add_argument("--cpu-experts", type=int, default=256,
                    help="experts whose rows the CPU oracle processes in its timed sample")
     p.add_argument("--no-row-major-ref", action="store_true",
@@ -77,27 +80,43 @@ def measured_traffic():
         return None
 
 
-def algorithmic(w, counts):
+def algorithmic(w, counts, fmt="bf16"):
     """Algorithmic HBM bytes and MFMA FLOPs of one layer call (and of the
-    gate/up kernel alone) from the realised routing histogram."""
+    gate/up kernel alone) from the realised routing histogram.  fp8 weights
+    are one byte per element plus an fp32 scale per row."""
     touched = int((counts > 0).sum())
     T, H, I, K = w.T, w.H, w.I, w.K
-    b_expert = 3 * H * I * 2                      # gate, up, down rows of one expert, bf16
+    if fmt == "fp8":
+        b_expert = 3 * H * I + (2 * I + H) * 4    # codes + per-row scales
+        b_gu = 2 * I * H + 2 * I * 4
+    else:
+        b_expert = 3 * H * I * 2                  # gate, up, down rows of one expert, bf16
+        b_gu = 2 * I * H * 2
     layer_bytes = touched * b_expert + w.E * H * 4 + T * H * 2 + T * H * 2
-    gu_bytes = touched * 2 * I * H * 2 + T * H * 2 + K * T * I * 2
+    gu_bytes = touched * b_gu + T * H * 2 + K * T * I * 2
     flops = K * T * 2 * 3 * H * I
     return {"touched": touched, "layer_bytes": layer_bytes, "gate_up_bytes": gu_bytes,
             "expert_flops": flops, "gate_up_flops": K * T * 2 * 2 * H * I}
 
 
-def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
-    """Times `steps` staged layer passes; returns timing dict and routing."""
+def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16"):
+    """Times `steps` staged layer passes; returns timing dict and routing.
+    fmt "bf16": fragment-packed bf16 expert weights; "fp8": E4M3FN codes
+    with per-row scales."""
     dev = wts["dev"]
     w = synth.workload(name)
     x = synth.make_x(w, args.seed, dev, w_router=wts["w_router"])
     wr, wgu, wd = wts["w_router"], wts["p_gate_up"], wts["p_down"]
     lay = gtr.LAYOUT_PACKED
     ws = gtr.Workspace()
+    f8 = wts.get("fp8")
+    if fmt == "fp8":
+        gate_up = lambda x, ps, o: gtr.expert_gate_up_fp8(x, ps, o, f8, workspace=ws)
+        down = lambda h, o: gtr.expert_down_fp8(h, o, f8, workspace=ws)
+    else:
+        gate_up = lambda x, ps, o: gtr.expert_gate_up(x, ps, o, wgu, weight_layout=lay,
+                                                      workspace=ws)
+        down = lambda h, o: gtr.expert_down(h, o, wd, weight_layout=lay, workspace=ws)
 
     def step(ev=None):
         if ev is not None:
@@ -108,10 +127,10 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
         c, o, ps, pd = gtr.permute(ids, workspace=ws)
         if ev is not None:
             ev[2].record()
-        h = gtr.expert_gate_up(x, ps, o, wgu, weight_layout=lay, workspace=ws)
+        h = gate_up(x, ps, o)
         if ev is not None:
             ev[3].record()
-        y = gtr.expert_down(h, o, wd, weight_layout=lay, workspace=ws)
+        y = down(h, o)
         if ev is not None:
             ev[4].record()
         out = gtr.combine(y, pd, tw)
@@ -142,9 +161,19 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch):
             gtr.layer_forward(x, wr, a, b, weight_layout=layout, workspace=ws)
         torch.cuda.synchronize()
         return (time.perf_counter() - t1) * 1e3 / steps
-    layer_ms = time_layer(wgu, wd, lay)
-    rowmajor_ms = (None if args.no_row_major_ref else
-                   time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
+    if fmt == "fp8":
+        for _ in range(2):
+            gtr.layer_forward_fp8(x, wr, f8, workspace=ws)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            gtr.layer_forward_fp8(x, wr, f8, workspace=ws)
+        torch.cuda.synchronize()
+        layer_ms, rowmajor_ms = (time.perf_counter() - t1) * 1e3 / steps, None
+    else:
+        layer_ms = time_layer(wgu, wd, lay)
+        rowmajor_ms = (None if args.no_row_major_ref else
+                       time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
             "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
             "counts": counts.cpu().numpy(), "ids": ids}
@@ -281,6 +310,34 @@ def main():
                             "touched_experts": da["touched"],
                             "stage_ms": {k: round(v, 4) for k, v in d["stage_ms"].items()}}
         del d
+    if not args.no_fp8:
+        # the FP8 per-channel variant of the same layer (weights quantised once
+        # at load time); reported beside the bf16 headline, never in `value`
+        print("[bench] quantising experts to fp8 and timing the fp8 variant", file=sys.stderr,
+              flush=True)
+        wts["fp8"] = gtr.quantize_fp8(wts["w_gate_up"], wts["w_down"])
+        torch.cuda.synchronize()
+        fp8 = {"weights": "E4M3FN codes + fp32 scale per output row; bf16 activations, "
+                          "fp32 accumulation",
+               "weight_bytes": wts["fp8"].nbytes()}
+        for name in ([args.workload] + ([] if args.no_decode or args.workload == "decode"
+                                        else ["decode"])):
+            f = run_workload(name, wts, args, args.steps if name == args.workload
+                             else max(args.steps, 10), 3, gtr, synth, torch, fmt="fp8")
+            fa = algorithmic(f["w"], f["counts"], "fp8")
+            fms, fgu = f["ms_per_step"], f["stage_ms"]["gate_up"]
+            fp8[name] = {"tokens": f["w"].T, "ms_per_step": round(fms, 4),
+                         "tokens_per_s": round(f["w"].T / (fms * 1e-3), 1),
+                         "layer_hbm_gbs": round(fa["layer_bytes"] / (fms * 1e-3) / 1e9, 1),
+                         "layer_hbm_frac": round(fa["layer_bytes"] / (fms * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBS, 4),
+                         "gate_up_gbs": round(fa["gate_up_bytes"] / (fgu * 1e-3) / 1e9, 1),
+                         "gate_up_frac": round(fa["gate_up_bytes"] / (fgu * 1e-3) / 1e9
+                                               / HBM_PEAK_GBS, 4),
+                         "layer_forward_ms": round(f["layer_forward_ms"], 4),
+                         "stage_ms": {k: round(v, 4) for k, v in f["stage_ms"].items()}}
+            del f
+        result["fp8"] = fp8
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, r["x"], wts, args.cpu_experts, torch)

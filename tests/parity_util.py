@@ -111,13 +111,18 @@ class OracleFp8Experts:
         self._cache = {}
 
     def quantized(self, e):
-        gu = np.asarray(self._gu[e] if not callable(self._gu) else self._gu(e), np.float32)
-        dn = np.asarray(self._dn[e] if not callable(self._dn) else self._dn(e), np.float32)
-        return oracle.quantize_fp8_per_channel(gu), oracle.quantize_fp8_per_channel(dn)
-
-    def __call__(self, e):
+        """((codes, scales) of gate_up, (codes, scales) of down) of expert e."""
         e = int(e)
         if e not in self._cache:
-            (qg, sg), (qd, sd) = self.quantized(e)
-            self._cache[e] = (oracle.dequantize_fp8(qg, sg), oracle.dequantize_fp8(qd, sd))
-        return self._cache[e]
+            gu = np.asarray(self._gu[e] if not callable(self._gu) else self._gu(e), np.float32)
+            dn = np.asarray(self._dn[e] if not callable(self._dn) else self._dn(e), np.float32)
+            self._cache[e] = (oracle.quantize_fp8_per_channel(gu),
+                              oracle.quantize_fp8_per_channel(dn), {})
+        return self._cache[e][:2]
+
+    def __call__(self, e):
+        (qg, sg), (qd, sd) = self.quantized(e)
+        deq = self._cache[int(e)][2]
+        if not deq:
+            deq["w"] = (oracle.dequantize_fp8(qg, sg), oracle.dequantize_fp8(qd, sd))
+        return deq["w"]

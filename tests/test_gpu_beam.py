@@ -7,7 +7,10 @@ launch configuration the benchmark times:
 * the permutation for every pair, exact;
 * the expert GEMMs on sampled experts' rows (the largest, a small and a
   median expert);
-* the whole layer on sampled tokens, each computed one by one by the oracle.
+* the whole layer on sampled tokens, each computed one by one by the oracle;
+* the same with FP8 per-channel weights, quantised on the device, against the
+  oracle's own quantisation of the sampled experts (codes and scales bit-exact,
+  outputs on the oracle's dequantised weights).
 """
 import numpy as np
 import pytest
@@ -16,7 +19,8 @@ import torch
 import grouped_top_routing_amd as gtr
 import oracle
 import synth
-from parity_util import assert_close, check_routing, say, to_np
+from parity_util import (OracleFp8Experts, assert_close, check_routing, say, to_np,
+                         unpack_fp8_codes)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -108,3 +112,61 @@ def test_beam_staged_calls_match_layer(beam):
     assert torch.equal(out, out2)
     y2 = gtr.expert_ffn(x, ps, o, beam["w_gate_up"], beam["w_down"])
     assert torch.equal(y, y2)
+
+
+@pytest.fixture(scope="module")
+def beam_fp8(beam):
+    say("[beam:fp8] quantising 256 experts on the device")
+    f = gtr.quantize_fp8(beam["w_gate_up"], beam["w_down"])
+    torch.cuda.synchronize()
+    ref = OracleFp8Experts(lambda e: to_np(beam["w_gate_up"][e]),
+                           lambda e: to_np(beam["w_down"][e]))
+    return f, ref
+
+
+def _check_fp8_expert(f, ref, e):
+    (qg, sg), (qd, sd) = ref.quantized(e)
+    assert np.array_equal(to_np(f.s_gate_up[e]).view(np.uint32), sg.view(np.uint32))
+    assert np.array_equal(to_np(f.s_down[e]).view(np.uint32), sd.view(np.uint32))
+    assert np.array_equal(unpack_fp8_codes(to_np(f.q_gate_up[e:e + 1]))[0], qg)
+    assert np.array_equal(unpack_fp8_codes(to_np(f.q_down[e:e + 1]))[0], qd)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_beam_layer_fp8(beam, beam_fp8, name):
+    f, ref = beam_fp8
+    w = synth.workload(name)
+    say(f"[beam:fp8:{name}] T={w.T} layer_forward_fp8")
+    x = synth.make_x(w, 0, DEV, w_router=beam["w_router"])
+    out, ids, wts = gtr.layer_forward_fp8(x, beam["w_router"], f, return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    # routing is the bf16 path's, bit for bit
+    out16, ids16, w16 = gtr.layer_forward(x, beam["w_router"], beam["w_gate_up"],
+                                          beam["w_down"], return_routing=True)
+    assert torch.equal(ids, ids16) and torch.equal(wts, w16)
+    xn = to_np(x)
+    say(f"[beam:fp8:{name}] oracle routing")
+    rr = oracle.route(xn, beam["wr_np"])
+    check_routing(to_np(ids), to_np(wts), rr)
+    rc, ro, rps, rpd = oracle.permute(rr.ids, 256)
+    y = gtr.expert_ffn_fp8(x, torch.from_numpy(rps.astype(np.int32)).to(DEV),
+                           torch.from_numpy(ro.astype(np.int32)).to(DEV), f)
+    # one sampled unflagged token: its 8 experts' codes and scales, their
+    # rows of the expert MLPs, and the layer output
+    rng = np.random.default_rng(1)
+    cand = np.nonzero(rr.margin >= oracle.MARGIN_TOL)[0]
+    t = int(rng.choice(cand))
+    outn = to_np(out)
+    acc = np.zeros(xn.shape[1])
+    for j, e in enumerate(rr.ids[t]):
+        e = int(e)
+        say(f"[beam:fp8:{name}] token {t} expert {e}")
+        _check_fp8_expert(f, ref, e)
+        gu, dn = ref(e)
+        r0, r1 = int(ro[e]), int(ro[e + 1])
+        r1 = min(r1, r0 + 192)
+        assert_close(to_np(y[r0:r1]), oracle.ffn_rows(xn[rps[r0:r1] // 8], gu, dn),
+                     f"y_perm expert {e} rows {r1 - r0}/{rc[e]}")
+        acc += rr.weights[t, j] * oracle.ffn_rows(xn[t:t + 1], gu, dn)[0]
+    assert_close(outn[t], 2.5 * acc, f"out token {t}")
