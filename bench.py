@@ -282,7 +282,7 @@ def main():
                                f"groups={w.G} kept={w.KG} topk={w.K}",
                    "tokens": w.T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
                    "seed": args.seed},
-        "roofline": {"kernel": "grouped_gemm_kernel (gate/up + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": "beam::stream_gemm_kernel, gate/up + SwiGLU instance", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if w.name == "prefill" else None,
