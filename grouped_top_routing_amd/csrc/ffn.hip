@@ -47,7 +47,7 @@ namespace beam {
 #define BEAM_GEMM_S8 5
 #endif
 #ifndef BEAM_GEMM_S12
-#define BEAM_GEMM_S12 5
+#define BEAM_GEMM_S12 4
 #endif
 #ifndef BEAM_GEMM_MAXMB
 #define BEAM_GEMM_MAXMB 12
@@ -57,6 +57,12 @@ namespace beam {
 #endif
 #ifndef BEAM_GEMM_NW12
 #define BEAM_GEMM_NW12 8
+#endif
+#ifndef BEAM_GEMM_RG8
+#define BEAM_GEMM_RG8 2
+#endif
+#ifndef BEAM_GEMM_RG12
+#define BEAM_GEMM_RG12 2
 #endif
 constexpr int kBKS = 32;                // k per pipeline stage (one MFMA k)
 constexpr int kFrag = 1024;             // bytes of one 16 x 32 bf16 MFMA operand
@@ -78,20 +84,37 @@ struct ItemArgs {
   int row0, nrows, ntile;
 };
 
-// One (m-tile, n-tile) item with exactly NRB live 16-row blocks.  MB sizes the
-// LDS ring; fragments of blocks NRB..MB-1 are not loaded.
-template <int NRB, int MB, int kNW, int NCBW, int S, bool SWIGLU>
-__device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int wave, int lane) {
+// Work split inside a workgroup: the kNW waves form RG row groups x CG = kNW /
+// RG column groups.  Every item covers 16 weight-row blocks (kColsGateUp gate
+// + up columns, or kColsDown down columns), so a wave owns NCBW = 16 / CG
+// column blocks and RB of the item's NRB row blocks.  With RG = 2 each A
+// fragment is read from LDS by half the waves and each B fragment by two,
+// which cuts LDS read traffic per MFMA against RG = 1 (every wave reading
+// every A fragment).
+constexpr int kItemBlocks = 16;
+
+// One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
+// this wave computes RB blocks starting at block row_off.  MB sizes the LDS
+// ring; fragments of blocks NRB..MB-1 are not loaded.
+template <int NRB, int RB, int MB, int kNW, int RG, int S, bool SWIGLU>
+__device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, int wave, int lane,
+                                               int row_off) {
+  constexpr int CG = kNW / RG;
+  constexpr int NCBW = kItemBlocks / CG;        // column blocks this wave computes
+  constexpr int NBL = NCBW / RG;                // ... and loads per stage (shared with its row peers)
   constexpr int D = S - 1;                      // stages in flight ahead of compute
-  constexpr int AOFF = kNW * NCBW * kFrag;      // slot = B fragments, then A fragments
+  constexpr int AOFF = kItemBlocks * kFrag;     // slot = B fragments, then A fragments
   constexpr int SLOT = AOFF + MB * kFrag;
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
-  constexpr int WCOLS = kNW * HALF * 16;
-  // A fragments of this wave: blocks wave, wave+4, ... below NRB
+  constexpr int WCOLS = CG * HALF * 16;
+  constexpr int RBX = RB > 0 ? RB : 1;
+  static_assert(CG * RG == kNW && NCBW * CG == kItemBlocks && NBL * RG == NCBW, "work split");
+  // A fragments this wave loads: blocks wave, wave + kNW, ... below NRB
   constexpr int AMAX = (NRB + kNW - 1) / kNW;
   const int r = lane & 15, g = lane >> 4;
+  const int cg = wave % CG, rg = wave / CG;
   const int nk = a.K / kBKS;
-  // Waves own different numbers of A fragments when NRB % 4 != 0, so each
+  // Waves own different numbers of A fragments when NRB % kNW != 0, so each
   // wave's loads per stage (and thus its vmcnt thresholds) are its own:
   // na in {AMAX - 1, AMAX}.  Both values are handled by separate waits.
   const int na = (NRB - wave + kNW - 1) / kNW;
@@ -104,43 +127,45 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
     const int src = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
     asrc[j] = a.A + (size_t)src * a.K + 8 * g;
   }
-  const uint16_t* bsrc[NCBW];
-#pragma unroll
-  for (int cb = 0; cb < NCBW; ++cb) {
-    int wrow;
+  // the weight row (output column) of lane r in column block cb of group cg
+  auto weight_row = [&](int cb) {
     if (SWIGLU) {
       const int j = cb % HALF;
-      wrow = a.ntile * WCOLS + wave * HALF * 16 + j * 16 + r + (cb >= HALF ? a.up_row0 : 0);
-    } else {
-      wrow = a.ntile * WCOLS + wave * NCBW * 16 + cb * 16 + r;
+      return a.ntile * WCOLS + cg * HALF * 16 + j * 16 + r + (cb >= HALF ? a.up_row0 : 0);
     }
+    return a.ntile * WCOLS + cg * NCBW * 16 + cb * 16 + r;
+  };
+  const uint16_t* bsrc[NBL];
+#pragma unroll
+  for (int t = 0; t < NBL; ++t) {
+    const int wrow = weight_row(rg + RG * t);
     // row-major: row wrow, k chunk 8g; packed: fragment (wrow/16, stage) holds
     // this lane's 16 bytes at lane*8, and a row block's fragments follow
     // each other along k.
-    bsrc[cb] = a.packed ? a.W + (size_t)((wrow - r) >> 4) * nk * kFragElems + lane * 8
-                        : a.W + (size_t)wrow * a.K + 8 * g;
+    bsrc[t] = a.packed ? a.W + (size_t)((wrow - r) >> 4) * nk * kFragElems + lane * 8
+                       : a.W + (size_t)wrow * a.K + 8 * g;
   }
   const int bstep = a.packed ? kFragElems : kBKS;  // elements per stage along a stream
   // LDS byte offset of the ring (addrspace cast, not the flat address)
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
-  const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds0 + wave * NCBW * kFrag);
+  const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds0 + (cg * NCBW + rg) * kFrag);
   const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds0 + AOFF + wave * kFrag);
 
   auto issue = [&](int st) {
     const uint32_t so = (uint32_t)((st % S) * SLOT);
     const int k0 = st * kBKS;
 #pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb)
-      lds_dma16(bsrc[cb] + (size_t)st * bstep, b_base + so + cb * kFrag);
+    for (int t = 0; t < NBL; ++t)
+      lds_dma16(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
 #pragma unroll
     for (int j = 0; j < AMAX; ++j)
       if (j < na) lds_dma16(asrc[j] + k0, a_base + so + kNW * j * kFrag);
   };
 
-  f32x4_t acc[NRB][NCBW];
+  f32x4_t acc[RBX][NCBW];
 #pragma unroll
-  for (int i = 0; i < NRB; ++i)
+  for (int i = 0; i < RBX; ++i)
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -152,38 +177,42 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
   // min(st + D - 1, nk - 1) have been issued
   auto wait_for = [&](int st) {
     const int ahead = min(D - 1, nk - 1 - st);
-    if (na == AMAX) wait_stage<D - 1, NCBW + AMAX>(ahead);
-    else wait_stage<D - 1, NCBW + AMAX - 1>(ahead);
+    if (na == AMAX) wait_stage<D - 1, NBL + AMAX>(ahead);
+    else wait_stage<D - 1, NBL + AMAX - 1>(ahead);
   };
-  auto read_frags = [&](int st, uint4 (&af)[NRB], uint4 (&bf)[NCBW]) {
+  auto read_frags = [&](int st, uint4 (&af)[RBX], uint4 (&bf)[NCBW]) {
     const uint8_t* sl = lds + (st % S) * SLOT;
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb)
-      bf[cb] = *reinterpret_cast<const uint4*>(sl + (wave * NCBW + cb) * kFrag + 16 * lane);
+      bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
+    if constexpr (RB > 0) {
 #pragma unroll
-    for (int i = 0; i < NRB; ++i)
-      af[i] = *reinterpret_cast<const uint4*>(sl + AOFF + i * kFrag + 16 * lane);
+      for (int i = 0; i < RB; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(sl + AOFF + (row_off + i) * kFrag + 16 * lane);
+    }
   };
   // One K-stage.  The next stage's fragments are read from LDS before this
   // stage's MFMAs are issued, so LDS latency hides behind matrix work.  Slot
   // reuse: stage kt + D refills the slot of stage kt - 1, whose fragments
   // every wave read (and waited for) before the previous barrier.
-  auto step = [&](int kt, uint4 (&ca)[NRB], uint4 (&cbf)[NCBW], uint4 (&na_)[NRB],
+  auto step = [&](int kt, uint4 (&ca)[RBX], uint4 (&cbf)[NCBW], uint4 (&na_)[RBX],
                   uint4 (&nb_)[NCBW]) {
     if (kt + D < nk) issue(kt + D);
     if (kt + 1 < nk) wait_for(kt + 1);
     wait_lgkm0();      // this wave's reads of stage kt have landed
     stage_barrier();   // stage kt + 1 is visible to every wave
     if (kt + 1 < nk) read_frags(kt + 1, na_, nb_);
+    if constexpr (RB > 0) {
 #pragma unroll
-    for (int i = 0; i < NRB; ++i)
+      for (int i = 0; i < RB; ++i)
 #pragma unroll
-      for (int cb = 0; cb < NCBW; ++cb)
-        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[i]), as_bf16x8(cbf[cb]),
-                                                             acc[i][cb], 0, 0, 0);
+        for (int cb = 0; cb < NCBW; ++cb)
+          acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(ca[i]), as_bf16x8(cbf[cb]), acc[i][cb], 0, 0, 0);
+    }
   };
 
-  uint4 a0[NRB], b0[NCBW], a1[NRB], b1[NCBW];
+  uint4 a0[RBX], b0[NCBW], a1[RBX], b1[NCBW];
   wait_for(0);
   stage_barrier();
   read_frags(0, a0, b0);
@@ -193,6 +222,7 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
     step(kt + 1, a1, b1, a0, b0);
   }
   if (kt < nk) step(kt, a0, b0, a1, b1);
+  wait_lgkm0();
   stage_barrier();  // every wave is done with the ring before the next item refills it
 
   // Epilogue through LDS (the ring is free after the barrier above): each
@@ -205,25 +235,27 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
   constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per tile row
   static_assert(16 * NRB * TSTRIDE * 2 <= S * SLOT, "epilogue tile fits the ring");
   uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
+  if constexpr (RB > 0) {
 #pragma unroll
-  for (int i = 0; i < NRB; ++i) {
+    for (int i = 0; i < RB; ++i) {
 #pragma unroll
-    for (int j = 0; j < HALF; ++j) {
-      const int col = wave * HALF * 16 + j * 16 + r;
+      for (int j = 0; j < HALF; ++j) {
+        const int col = cg * HALF * 16 + j * 16 + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = i * 16 + 4 * g + v;
-        float o;
-        if (SWIGLU) {
-          const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
-          o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
-        } else {
-          o = acc[i][j][v];
+        for (int v = 0; v < 4; ++v) {
+          const int row = (row_off + i) * 16 + 4 * g + v;
+          float o;
+          if (SWIGLU) {
+            const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
+            o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+          } else {
+            o = acc[i][j][v];
+          }
+          const uint32_t b = f32_to_bf16(o);
+          const uint32_t nb = __shfl_xor(b, 1);
+          if ((r & 1) == 0)
+            *reinterpret_cast<uint32_t*>(tile + row * TSTRIDE + col) = b | (nb << 16);
         }
-        const uint32_t b = f32_to_bf16(o);
-        const uint32_t nb = __shfl_xor(b, 1);
-        if ((r & 1) == 0)
-          *reinterpret_cast<uint32_t*>(tile + row * TSTRIDE + col) = b | (nb << 16);
       }
     }
   }
@@ -241,24 +273,40 @@ __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int w
   stage_barrier();  // the tile is read out before the next item refills the ring
 }
 
-template <int N, int MB, int kNW, int NCBW, int S, bool SWIGLU>
+// Item with NRB live row blocks: row group 0 takes the first ceil(NRB / RG)
+// blocks, row group 1 the rest.
+template <int NRB, int MB, int kNW, int RG, int S, bool SWIGLU>
+__device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int wave, int lane) {
+  if constexpr (RG == 1) {
+    gemm_item_rows<NRB, NRB, MB, kNW, 1, S, SWIGLU>(a, lds, wave, lane, 0);
+  } else {
+    static_assert(RG == 2, "one or two row groups");
+    constexpr int RB0 = (NRB + 1) / 2;
+    if (wave < kNW / 2)
+      gemm_item_rows<NRB, RB0, MB, kNW, 2, S, SWIGLU>(a, lds, wave, lane, 0);
+    else
+      gemm_item_rows<NRB, NRB - RB0, MB, kNW, 2, S, SWIGLU>(a, lds, wave, lane, RB0);
+  }
+}
+
+template <int N, int MB, int kNW, int RG, int S, bool SWIGLU>
 __device__ __forceinline__ void gemm_item_dispatch(int nrb, const ItemArgs& a, uint8_t* lds,
                                                    int wave, int lane) {
   if constexpr (N > MB) {
     return;
   } else {
-    if (nrb == N) gemm_item<N, MB, kNW, NCBW, S, SWIGLU>(a, lds, wave, lane);
-    else gemm_item_dispatch<N + 1, MB, kNW, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
+    if (nrb == N) gemm_item<N, MB, kNW, RG, S, SWIGLU>(a, lds, wave, lane);
+    else gemm_item_dispatch<N + 1, MB, kNW, RG, S, SWIGLU>(nrb, a, lds, wave, lane);
   }
 }
 
-template <int MB, int kNW, int NCBW, int S, bool SWIGLU>
+template <int MB, int kNW, int RG, int S, bool SWIGLU>
 __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
     const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed) {
-  constexpr int SLOT = (kNW * NCBW + MB) * kFrag;
-  constexpr int WCOLS = kNW * (SWIGLU ? NCBW / 2 : NCBW) * 16;
+  constexpr int SLOT = (kItemBlocks + MB) * kFrag;
+  constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S * SLOT];
 
@@ -280,7 +328,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0, packed,
                plan_row0[tile], plan_rows[tile], q - tile * nt_n};
     const int nrb = (a.nrows + 15) >> 4;
-    gemm_item_dispatch<1, MB, kNW, NCBW, S, SWIGLU>(nrb, a, lds, wave, lane);
+    gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU>(nrb, a, lds, wave, lane);
   }
 }
 
@@ -345,15 +393,16 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Launch configurations (MB, waves, NCBW, S).  LDS per workgroup =
-// S * (waves * NCBW + MB) KB.  Small m-tiles use 4 waves and fit two
-// workgroups per CU; large ones use 8 waves (two per SIMD) in one workgroup.
-template <int MB, int NW, int NCBW, int S, bool SWIGLU>
+// Launch configurations (MB, waves, row groups, S).  LDS per workgroup =
+// S * (16 + MB) KB.  Small m-tiles use 4 waves and fit two workgroups per CU;
+// large ones use 8 waves (two per SIMD) in one workgroup, as 2 row groups x 4
+// column groups.
+template <int MB, int NW, int RG, int S, bool SWIGLU>
 static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int topk,
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                 int packed, int64_t max_items, hipStream_t stream) {
-  auto kern = stream_gemm_kernel<MB, NW, NCBW, S, SWIGLU>;
+  auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU>;
   static int per_cu = 0;  // resident workgroups per CU, fixed per build
   static int cus = 0;
   if (per_cu == 0) {
@@ -384,7 +433,7 @@ int ffn_choose_mb(int64_t rows, int E) {
   const int64_t mean = rows / (E > 0 ? E : 1);
   if (mean <= 40) return 4;
   if (mean <= 80 || BEAM_GEMM_MAXMB == 8) return 8;
-  return 12;
+  return BEAM_GEMM_MAXMB;
 }
 
 int ffn_out_cols_per_item(bool swiglu) { return swiglu ? kColsGateUp : kColsDown; }
@@ -409,20 +458,20 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                int packed, int64_t max_items, hipStream_t stream) {
-#define BEAM_STREAM_CASE(MBV, NWV, NCBWV, SV)                                                   \
+#define BEAM_STREAM_CASE(MBV, NWV, RGV, SV)                                                     \
   case MBV:                                                                                     \
-    return swiglu ? launch_stream<MBV, NWV, NCBWV, SV, true>(A, gather, topk, W, wstride, C,    \
-                                                             plan, max_tiles, K, n_out,         \
-                                                             up_row0, packed, max_items,        \
-                                                             stream)                            \
-                  : launch_stream<MBV, NWV, NCBWV, SV, false>(A, gather, topk, W, wstride, C,   \
-                                                              plan, max_tiles, K, n_out,        \
-                                                              up_row0, packed, max_items,       \
-                                                              stream);
+    return swiglu ? launch_stream<MBV, NWV, RGV, SV, true>(A, gather, topk, W, wstride, C,      \
+                                                           plan, max_tiles, K, n_out, up_row0,  \
+                                                           packed, max_items, stream)           \
+                  : launch_stream<MBV, NWV, RGV, SV, false>(A, gather, topk, W, wstride, C,     \
+                                                            plan, max_tiles, K, n_out, up_row0, \
+                                                            packed, max_items, stream);
   switch (mb) {
-    BEAM_STREAM_CASE(4, 4, 4, BEAM_GEMM_S4)
-    BEAM_STREAM_CASE(8, BEAM_GEMM_NW8, 16 / BEAM_GEMM_NW8, BEAM_GEMM_S8)
-    BEAM_STREAM_CASE(12, BEAM_GEMM_NW12, 16 / BEAM_GEMM_NW12, BEAM_GEMM_S12)
+    BEAM_STREAM_CASE(4, 4, 1, BEAM_GEMM_S4)
+    BEAM_STREAM_CASE(8, BEAM_GEMM_NW8, BEAM_GEMM_RG8, BEAM_GEMM_S8)
+#if BEAM_GEMM_MAXMB != 8
+    BEAM_STREAM_CASE(BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12, BEAM_GEMM_S12)
+#endif
     default:
       return hipErrorInvalidValue;
   }

@@ -334,6 +334,20 @@ int ffn_fp8_choose_mb(int64_t rows, int E) {
   return 12;
 }
 
+// Pipeline shapes (waves, stages) of the 128- and 192-row configurations.
+#ifndef BEAM_FP8_NW8
+#define BEAM_FP8_NW8 8
+#endif
+#ifndef BEAM_FP8_S8
+#define BEAM_FP8_S8 3
+#endif
+#ifndef BEAM_FP8_NW12
+#define BEAM_FP8_NW12 8
+#endif
+#ifndef BEAM_FP8_S12
+#define BEAM_FP8_S12 3
+#endif
+
 hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                    int topk, const uint8_t* Q, const float* scales, int64_t qstride,
                                    int N, uint16_t* C, const int32_t* plan, int max_tiles, int K,
@@ -348,8 +362,8 @@ hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const
                                                            up_row0, max_items, stream);
   switch (mb) {
     BEAM_FP8_CASE(2, 4, 4, 4)
-    BEAM_FP8_CASE(8, 8, 2, 3)
-    BEAM_FP8_CASE(12, 8, 2, 3)
+    BEAM_FP8_CASE(8, BEAM_FP8_NW8, 16 / BEAM_FP8_NW8, BEAM_FP8_S8)
+    BEAM_FP8_CASE(12, BEAM_FP8_NW12, 16 / BEAM_FP8_NW12, BEAM_FP8_S12)
     default:
       return hipErrorInvalidValue;
   }
