@@ -47,7 +47,8 @@ __all__ = [
     "RouteResult", "route", "route_replay", "select", "router_logits", "sigmoid_f32",
     "permute", "expert_ffn", "ffn_rows", "combine", "layer_forward",
     "selection_admissible", "MARGIN_TOL", "E4M3_MAX", "e4m3_encode", "e4m3_decode",
-    "quantize_fp8_per_channel", "dequantize_fp8",
+    "quantize_fp8_per_channel", "dequantize_fp8", "LORA_RANK", "LORA_ALPHA", "lora_scale",
+    "ffn_rows_lora",
 ]
 
 #: Selection margin under which GPU and oracle may legitimately disagree.
@@ -174,12 +175,53 @@ def ffn_rows(x_rows, w_gate_up, w_down):
     return h @ np.asarray(w_down, dtype=np.float64).T
 
 
-def expert_ffn(x, perm_src, offsets, experts, topk=8):
+# ---------------------------------------------------------------------------
+# Expert LoRA ("Beam 1.0" miles recipes, section 5.5 "LoRA": an adapter on
+# each routed expert with rank 16, alpha 32, dropout 0, the router frozen;
+# the Axolotl Beam guide: LoRA on the fused expert weights).  Each adapted
+# weight W [out, in] gains W x + (alpha / rank) * B (A x) with A [rank, in]
+# and B [out, rank]; the fused gate/up weight carries one adapter
+# (A [rank, H], B [2I, rank]) and the down weight another (A [rank, I],
+# B [H, rank]).
+# ---------------------------------------------------------------------------
+LORA_RANK = 16
+LORA_ALPHA = 32
+
+
+def lora_scale(alpha=LORA_ALPHA, rank=LORA_RANK):
+    """The adapter's output multiplier alpha / rank (2.0 for Beam's recipe)."""
+    return float(alpha) / float(rank)
+
+
+def ffn_rows_lora(x_rows, w_gate_up, w_down, lora, scale):
+    """ffn_rows with one LoRA adapter on each expert weight, fp64 throughout:
+    [g | u] = X Wgu^T + s (X Agu^T) Bgu^T, h = SiLU(g) * u,
+    y = h Wd^T + s (h Ad^T) Bd^T.  ``lora`` = (a_gate_up, b_gate_up, a_down,
+    b_down) of this expert."""
+    X = np.asarray(x_rows, dtype=np.float64)
+    a_gu, b_gu, a_d, b_d = (np.asarray(t, dtype=np.float64) for t in lora)
+    gu = np.asarray(w_gate_up, dtype=np.float64)
+    inter = gu.shape[0] // 2
+    z = X @ gu.T + scale * ((X @ a_gu.T) @ b_gu.T)
+    g, u = z[:, :inter], z[:, inter:]
+    with np.errstate(over="ignore"):
+        h = g / (1.0 + np.exp(-g)) * u
+    return h @ np.asarray(w_down, dtype=np.float64).T + scale * ((h @ a_d.T) @ b_d.T)
+
+
+def expert_ffn(x, perm_src, offsets, experts, topk=8, lora=None, lora_scale_=None):
     """All experts over the permuted rows.  ``experts`` is either a pair of
-    arrays ([E, 2I, H], [E, H, I]) or a callable ``e -> (gate_up, down)``.
+    arrays ([E, 2I, H], [E, H, I]) or a callable ``e -> (gate_up, down)``;
+    ``lora`` (optional) is a 4-tuple of arrays ([E, r, H], [E, 2I, r],
+    [E, r, I], [E, H, r]) or a callable ``e -> 4-tuple``, applied with the
+    multiplier ``lora_scale_`` (default alpha / rank of Beam's recipe).
     Returns y_perm, fp64 [T*k, H], row r belonging to slot perm_src[r]."""
     x = np.asarray(x)
     get = experts if callable(experts) else (lambda e: (experts[0][e], experts[1][e]))
+    if lora is not None and not callable(lora):
+        arrs = lora
+        lora = lambda e: tuple(t[e] for t in arrs)
+    s = lora_scale() if lora_scale_ is None else lora_scale_
     y = np.zeros((len(perm_src), x.shape[1]), dtype=np.float64)
     for e in range(len(offsets) - 1):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
@@ -187,7 +229,10 @@ def expert_ffn(x, perm_src, offsets, experts, topk=8):
             continue  # an expert that receives no token does no work
         tokens = np.asarray(perm_src[r0:r1]) // topk
         gu, dn = get(e)
-        y[r0:r1] = ffn_rows(x[tokens], gu, dn)
+        if lora is None:
+            y[r0:r1] = ffn_rows(x[tokens], gu, dn)
+        else:
+            y[r0:r1] = ffn_rows_lora(x[tokens], gu, dn, lora(e), s)
     return y
 
 
@@ -199,9 +244,11 @@ def combine(y_perm, perm_dst, weights, scale=2.5):
 
 
 def layer_forward(x, w_router, experts, *, n_groups=8, topk_groups=4, topk=8,
-                  renormalize=True, scale=2.5, sel_bias=None, ids=None):
+                  renormalize=True, scale=2.5, sel_bias=None, ids=None, lora=None,
+                  lora_scale_=None):
     """The whole block: route, permute, expert MLPs, weighted combine.
-    With ``ids`` given, routing is replayed instead of selected."""
+    With ``ids`` given, routing is replayed instead of selected; ``lora`` adds
+    the expert adapters (see expert_ffn)."""
     E = np.asarray(w_router).shape[0]
     if ids is None:
         rr = route(x, w_router, n_groups=n_groups, topk_groups=topk_groups, topk=topk,
@@ -211,7 +258,8 @@ def layer_forward(x, w_router, experts, *, n_groups=8, topk_groups=4, topk=8,
         rr = None
         weights, _ = route_replay(x, w_router, ids, renormalize=renormalize)
     counts, offsets, perm_src, perm_dst = permute(ids, E)
-    y = expert_ffn(x, perm_src, offsets, experts, topk=ids.shape[1])
+    y = expert_ffn(x, perm_src, offsets, experts, topk=ids.shape[1], lora=lora,
+                   lora_scale_=lora_scale_)
     out = combine(y, perm_dst, weights, scale)
     return {"route": rr, "ids": ids, "weights": weights, "counts": counts, "offsets": offsets,
             "perm_src": perm_src, "perm_dst": perm_dst, "y_perm": y, "out": out}
