@@ -10,7 +10,8 @@ All computation happens in the HIP kernels of ``libbeam_moe.so`` (C ABI in
 include/beam_moe.h); this package only marshals torch tensors into it.
 """
 from ._lib import (  # noqa: F401
-    ENTRY_EXPERT_FFN, ENTRY_EXPERT_STAGE, ENTRY_LAYER, ENTRY_PERMUTE, ENTRY_ROUTE, EXPORTS,
+    ENTRY_EXPERT_FFN, ENTRY_EXPERT_FFN_LORA, ENTRY_EXPERT_STAGE, ENTRY_LAYER, ENTRY_LAYER_LORA,
+    ENTRY_PERMUTE, ENTRY_ROUTE, EXPORTS, LoraWeights, MoeLora, expert_ffn_lora, layer_forward_lora,
     LAYOUT_FP8_PACKED, LAYOUT_PACKED, LAYOUT_ROW_MAJOR, LIB_PATH, Fp8Weights, MoeConfig,
     MoeError, Workspace, combine, expert_down, expert_down_fp8, expert_ffn, expert_ffn_fp8,
     expert_gate_up, expert_gate_up_fp8, layer_forward, layer_forward_fp8, lib, make_config,

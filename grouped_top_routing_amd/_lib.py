@@ -26,6 +26,8 @@ ENTRY_PERMUTE = 1
 ENTRY_EXPERT_FFN = 2
 ENTRY_LAYER = 3
 ENTRY_EXPERT_STAGE = 4
+ENTRY_EXPERT_FFN_LORA = 5
+ENTRY_LAYER_LORA = 6
 
 LAYOUT_ROW_MAJOR = 0
 LAYOUT_PACKED = 1
@@ -36,7 +38,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_replay", "moe_permute"
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
            "moe_layer_forward", "moe_pack_weights", "moe_quantize_fp8", "moe_expert_ffn_fp8",
            "moe_expert_gate_up_fp8", "moe_expert_down_fp8", "moe_layer_forward_fp8",
-           "moe_status_string")
+           "moe_expert_ffn_lora", "moe_layer_forward_lora", "moe_status_string")
 
 
 class MoeConfig(ctypes.Structure):
@@ -51,6 +53,17 @@ class MoeConfig(ctypes.Structure):
         ("renormalize", ctypes.c_int32),
         ("routed_scaling", ctypes.c_float),
         ("weight_layout", ctypes.c_int32),
+    ]
+
+
+class MoeLora(ctypes.Structure):
+    _fields_ = [
+        ("a_gate_up", ctypes.c_void_p),
+        ("b_gate_up", ctypes.c_void_p),
+        ("a_down", ctypes.c_void_p),
+        ("b_down", ctypes.c_void_p),
+        ("rank", ctypes.c_int32),
+        ("scale", ctypes.c_float),
     ]
 
 
@@ -88,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_gate_up_fp8.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
         L.moe_expert_down_fp8.argtypes = [CP, P, P, P, P, P, P, Z, P]
         L.moe_layer_forward_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        LP = ctypes.POINTER(MoeLora)
+        L.moe_expert_ffn_lora.argtypes = [CP, P, P, P, P, P, LP, P, P, Z, P]
+        L.moe_layer_forward_lora.argtypes = [CP, P, P, P, P, P, LP, P, P, P, P, Z, P]
         L.moe_status_string.argtypes = [I]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -492,4 +508,90 @@ def layer_forward_fp8(x, w_router, w: Fp8Weights, *, sel_bias=None, num_groups=8
         ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(w.q_gate_up),
         _ptr(w.s_gate_up), _ptr(w.q_down), _ptr(w.s_down), _ptr(out), _ptr(ids), _ptr(tw),
         _ptr(ws), nb, _stream(x.device)))
+    return (out, ids, tw) if return_routing else out
+
+
+# ---------------------------------------------------------------------------
+# Expert LoRA on the bf16 expert weights
+class LoraWeights:
+    """One adapter per expert weight: a_gate_up [E, r, H], b_gate_up [E, 2I, r],
+    a_down [E, r, I], b_down [E, H, r] (bf16), applied as W a + scale * B (A a)."""
+
+    def __init__(self, a_gate_up, b_gate_up, a_down, b_down, scale):
+        self.a_gate_up, self.b_gate_up = a_gate_up, b_gate_up
+        self.a_down, self.b_down = a_down, b_down
+        self.scale = float(scale)
+
+    @property
+    def rank(self):
+        return int(self.a_gate_up.shape[1])
+
+    def check(self, E, H, I, device):
+        r = self.rank
+        _check(self.a_gate_up, "a_gate_up", torch.bfloat16, (E, r, H), device)
+        _check(self.b_gate_up, "b_gate_up", torch.bfloat16, (E, 2 * I, r), device)
+        _check(self.a_down, "a_down", torch.bfloat16, (E, r, I), device)
+        _check(self.b_down, "b_down", torch.bfloat16, (E, H, r), device)
+
+    def struct(self):
+        return MoeLora(self.a_gate_up.data_ptr(), self.b_gate_up.data_ptr(),
+                       self.a_down.data_ptr(), self.b_down.data_ptr(), self.rank, self.scale)
+
+
+def expert_ffn_lora(x, perm_src, offsets, w_gate_up, w_down, lora: LoraWeights, *, topk=8,
+                    weight_layout=LAYOUT_ROW_MAJOR, workspace=None):
+    """expert_ffn with expert LoRA: y_perm bf16 [T*k, H]."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    _check(x, "x", torch.bfloat16)
+    _check(perm_src, "perm_src", torch.int32, (T * topk,), x.device)
+    _check(offsets, "offsets", torch.int32, (E + 1,), x.device)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), x.device)
+    lora.check(E, H, I, x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=1, topk_groups=1, topk=topk,
+                      weight_layout=weight_layout)
+    y = torch.empty(T * topk, H, dtype=torch.bfloat16, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_EXPERT_FFN_LORA)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    ls = lora.struct()
+    _call("moe_expert_ffn_lora", lib().moe_expert_ffn_lora(
+        ctypes.byref(cfg), _ptr(x), _ptr(perm_src), _ptr(offsets), _ptr(w_gate_up), _ptr(w_down),
+        ctypes.byref(ls), _ptr(y), _ptr(ws), nb, _stream(x.device)))
+    return y
+
+
+def layer_forward_lora(x, w_router, w_gate_up, w_down, lora: LoraWeights, *, sel_bias=None,
+                       num_groups=8, topk_groups=4, topk=8, renormalize=True, routed_scaling=2.5,
+                       weight_layout=LAYOUT_ROW_MAJOR, return_routing=False, out=None,
+                       workspace=None):
+    """layer_forward with expert LoRA."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    _check(x, "x", torch.bfloat16)
+    _check(w_router, "w_router", torch.float32, (E, H), x.device)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), x.device)
+    lora.check(E, H, I, x.device)
+    if sel_bias is not None:
+        _check(sel_bias, "sel_bias", torch.float32, (E,), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=num_groups, topk_groups=topk_groups,
+                      topk=topk, renormalize=renormalize, routed_scaling=routed_scaling,
+                      weight_layout=weight_layout)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    else:
+        _check(out, "out", torch.bfloat16, (T, H), x.device)
+    ids = tw = None
+    if return_routing:
+        ids = torch.empty(T, topk, dtype=torch.int32, device=x.device)
+        tw = torch.empty(T, topk, dtype=torch.float32, device=x.device)
+    nb = workspace_bytes(cfg, ENTRY_LAYER_LORA)
+    ws = _ws(workspace, x.device).get(nb, x.device)
+    ls = lora.struct()
+    _call("moe_layer_forward_lora", lib().moe_layer_forward_lora(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(w_gate_up), _ptr(w_down),
+        ctypes.byref(ls), _ptr(out), _ptr(ids), _ptr(tw), _ptr(ws), nb, _stream(x.device)))
     return (out, ids, tw) if return_routing else out

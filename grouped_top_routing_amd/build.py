@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbeam_moe.so")
-SOURCES = ["capi.hip", "route.hip", "permute.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip"]
+SOURCES = ["capi.hip", "route.hip", "permute.hip", "ffn.hip", "ffn_fp8.hip", "lora.hip", "combine.hip"]
 ARCH = "gfx950"
 
 

@@ -75,12 +75,19 @@ size_t plan_bytes(const moe_config_t* c) {
 size_t ffn_ws(const moe_config_t* c) {
   return plan_bytes(c) + align_up((size_t)pairs(c) * c->intermediate * sizeof(uint16_t));
 }
+// LoRA intermediates t_gate_up and t_down [pairs, rank] bf16, sized for the
+// largest supported rank
+constexpr int kMaxLoraRank = 64;
+size_t lora_t_bytes(const moe_config_t* c) {
+  return align_up((size_t)pairs(c) * kMaxLoraRank * sizeof(uint16_t));
+}
+size_t ffn_lora_ws(const moe_config_t* c) { return ffn_ws(c) + 2 * lora_t_bytes(c); }
 
 struct LayerLayout {
   size_t ids, w, counts, offsets, psrc, pdst, y, scratch, total;
 };
 
-LayerLayout layer_layout(const moe_config_t* c) {
+LayerLayout layer_layout(const moe_config_t* c, bool lora = false) {
   LayerLayout L{};
   const size_t n = (size_t)pairs(c);
   size_t o = 0;
@@ -94,7 +101,8 @@ LayerLayout layer_layout(const moe_config_t* c) {
   L.scratch = o;
   size_t s = route_ws(c);
   if (permute_ws(c) > s) s = permute_ws(c);
-  if (ffn_ws(c) > s) s = ffn_ws(c);
+  const size_t f = lora ? ffn_lora_ws(c) : ffn_ws(c);
+  if (f > s) s = f;
   o += s;
   L.total = o;
   return L;
@@ -138,22 +146,23 @@ int do_plan(const moe_config_t* c, const int32_t* offsets, int32_t* plan, int mb
 }
 
 int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
-               const int32_t* plan, const uint16_t* wgu, uint16_t* h, hipStream_t s) {
+               const int32_t* plan, const uint16_t* wgu, uint16_t* h, hipStream_t s,
+               const LoraArgs& lora = LoraArgs{}) {
   const int64_t max_tiles = max_tiles_for(c);
   const int H = c->hidden, I = c->intermediate;
   return hip_status(launch_grouped_gemm(mb_for(c), true, x, psrc, c->topk, wgu,
                                         (int64_t)2 * I * H, h, plan, (int)max_tiles, H, I, I,
-                                        c->weight_layout,
+                                        c->weight_layout, lora,
                                         max_tiles * (I / ffn_out_cols_per_item(true)), s));
 }
 
 int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint16_t* wd,
-            uint16_t* y, hipStream_t s) {
+            uint16_t* y, hipStream_t s, const LoraArgs& lora = LoraArgs{}) {
   const int64_t max_tiles = max_tiles_for(c);
   const int H = c->hidden, I = c->intermediate;
   return hip_status(launch_grouped_gemm(mb_for(c), false, h, nullptr, c->topk, wd,
                                         (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0,
-                                        c->weight_layout,
+                                        c->weight_layout, lora,
                                         max_tiles * (H / ffn_out_cols_per_item(false)), s));
 }
 
@@ -165,6 +174,43 @@ int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const 
   if (st) return st;
   if ((st = do_gate_up(c, x, psrc, plan, wgu, h, s))) return st;
   return do_down(c, h, plan, wd, y, s);
+}
+
+// ---- expert LoRA on the bf16 expert weights ----
+bool lora_ok(const moe_lora_t* l) {
+  if (!l) return false;
+  if (l->rank != 16 && l->rank != 32 && l->rank != 48 && l->rank != 64) return false;
+  if (!std::isfinite(l->scale)) return false;
+  return l->a_gate_up && l->b_gate_up && l->a_down && l->b_down && aligned16(l->a_gate_up) &&
+         aligned16(l->b_gate_up) && aligned16(l->a_down) && aligned16(l->b_down);
+}
+
+// plan, t_gate_up = s x A_gu^T, gate/up (+ t_gate_up B_gu^T), t_down = s h A_d^T,
+// down (+ t_down B_d^T)
+int do_ffn_lora(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
+                const int32_t* offsets, const uint16_t* wgu, const uint16_t* wd,
+                const moe_lora_t* l, uint16_t* y, void* scratch, hipStream_t s) {
+  char* base = static_cast<char*>(scratch);
+  int32_t* plan = reinterpret_cast<int32_t*>(base);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + plan_bytes(c));
+  uint16_t* t_gu = reinterpret_cast<uint16_t*>(base + ffn_ws(c));
+  uint16_t* t_d = reinterpret_cast<uint16_t*>(base + ffn_ws(c) + lora_t_bytes(c));
+  const int H = c->hidden, I = c->intermediate, R = l->rank;
+  const int max_tiles = (int)max_tiles_for(c);
+  int st = do_plan(c, offsets, plan, mb_for(c), s);
+  if (st) return st;
+  if ((st = hip_status(launch_lora_a(x, psrc, c->topk, l->a_gate_up, H, R, l->scale, t_gu, plan,
+                                     max_tiles, s))))
+    return st;
+  LoraArgs lg;
+  lg.t = t_gu; lg.b = l->b_gate_up; lg.b_stride = (int64_t)2 * I * R; lg.rank = R;
+  if ((st = do_gate_up(c, x, psrc, plan, wgu, h, s, lg))) return st;
+  if ((st = hip_status(launch_lora_a(h, nullptr, c->topk, l->a_down, I, R, l->scale, t_d, plan,
+                                     max_tiles, s))))
+    return st;
+  LoraArgs ld;
+  ld.t = t_d; ld.b = l->b_down; ld.b_stride = (int64_t)H * R; ld.rank = R;
+  return do_down(c, h, plan, wd, y, s, ld);
 }
 
 // ---- fp8 expert weights ----
@@ -214,8 +260,9 @@ bool fp8_weights_ok(const uint8_t* q, const float* sc) {
 template <class Ffn>
 int layer_common(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
                  const float* sel_bias, uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
-                 void* workspace, size_t workspace_bytes, hipStream_t s, Ffn ffn) {
-  const LayerLayout L = layer_layout(cfg);
+                 void* workspace, size_t workspace_bytes, hipStream_t s, Ffn ffn,
+                 bool lora = false) {
+  const LayerLayout L = layer_layout(cfg, lora);
   int st = check_ws(workspace, workspace_bytes, L.total);
   if (st) return st;
   if (cfg->num_tokens == 0) return MOE_OK;
@@ -271,6 +318,8 @@ int moe_workspace_bytes(const moe_config_t* cfg, int entry, size_t* bytes) {
     case MOE_ENTRY_EXPERT_FFN: *bytes = ffn_ws(cfg); break;
     case MOE_ENTRY_LAYER: *bytes = layer_layout(cfg).total; break;
     case MOE_ENTRY_EXPERT_STAGE: *bytes = plan_bytes(cfg); break;
+    case MOE_ENTRY_EXPERT_FFN_LORA: *bytes = ffn_lora_ws(cfg); break;
+    case MOE_ENTRY_LAYER_LORA: *bytes = layer_layout(cfg, true).total; break;
     default: return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
@@ -553,6 +602,43 @@ int moe_layer_forward_fp8(const moe_config_t* cfg, const uint16_t* x, const floa
                       [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* scratch) {
                         return do_ffn_fp8(cfg, x, psrc, offsets, w, y, scratch, s);
                       });
+}
+
+int moe_expert_ffn_lora(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                        const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
+                        const moe_lora_t* lora, uint16_t* y_perm, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!x || !perm_src || !offsets || !w_gate_up || !w_down || !y_perm || !lora_ok(lora))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y_perm) ||
+      !aligned4(perm_src) || !aligned4(offsets))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(workspace, workspace_bytes, ffn_lora_ws(cfg)))) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if ((st = device_ready())) return st;
+  return do_ffn_lora(cfg, x, perm_src, offsets, w_gate_up, w_down, lora, y_perm, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_forward_lora(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                           const float* sel_bias, const uint16_t* w_gate_up,
+                           const uint16_t* w_down, const moe_lora_t* lora, uint16_t* out,
+                           int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!layer_args_ok(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out) || !w_gate_up ||
+      !w_down || !aligned16(w_gate_up) || !aligned16(w_down) || !lora_ok(lora))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return layer_common(
+      cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out, workspace, workspace_bytes, s,
+      [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* scratch) {
+        return do_ffn_lora(cfg, x, psrc, offsets, w_gate_up, w_down, lora, y, scratch, s);
+      },
+      true);
 }
 
 }  // extern "C"

@@ -82,6 +82,13 @@ struct ItemArgs {
   int K, n_out, up_row0;
   int packed;              // 1: W is in fragment order (see pack_weights_kernel)
   int row0, nrows, ntile;
+  // Optional expert LoRA, second factor: acc += t_r . Lb_e^T before the
+  // epilogue, with t [rows, lora_r] (already scaled, permuted row order) and
+  // this expert's Lb [n_total, lora_r], both bf16 row-major.  lora_t == null:
+  // no adapter.
+  const uint16_t* lora_t;
+  const uint16_t* lora_b;
+  int lora_r;
 };
 
 // Work split inside a workgroup: the kNW waves form RG row groups x CG = kNW /
@@ -225,6 +232,32 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   wait_lgkm0();
   stage_barrier();  // every wave is done with the ring before the next item refills it
 
+  // LoRA second factor: rank steps of 32 (ranks past lora_r contribute zeros),
+  // operands loaded straight from global memory in the MFMA lane order.
+  if constexpr (RB > 0) {
+    if (a.lora_t) {
+      const int R = a.lora_r;
+      for (int k0 = 0; k0 < R; k0 += 32) {
+        const bool live = k0 + 8 * g < R;
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+        uint4 bl[NCBW];
+#pragma unroll
+        for (int cb = 0; cb < NCBW; ++cb)
+          bl[cb] = live ? ld16(a.lora_b + (size_t)weight_row(cb) * R + k0 + 8 * g) : zero;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          int row = (row_off + i) * 16 + r;
+          row = row < a.nrows ? row : a.nrows - 1;
+          const uint4 al = live ? ld16(a.lora_t + (size_t)(a.row0 + row) * R + k0 + 8 * g) : zero;
+#pragma unroll
+          for (int cb = 0; cb < NCBW; ++cb)
+            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bl[cb]),
+                                                                 acc[i][cb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
   // Epilogue through LDS (the ring is free after the barrier above): each
   // wave writes its accumulators as bf16 into a row-major tile -- lane holds
   // rows 4g..4g+3 of column r of each 16x16 block; even lanes pair up with
@@ -304,7 +337,9 @@ template <int MB, int kNW, int RG, int S, bool SWIGLU>
 __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed) {
+    const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed,
+    const uint16_t* __restrict__ lora_t, const uint16_t* __restrict__ lora_b,
+    int64_t lora_b_stride, int lora_r) {
   constexpr int SLOT = (kItemBlocks + MB) * kFrag;
   constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
@@ -326,7 +361,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const int tile = q / nt_n;
     const int e = plan_expert[tile];
     ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0, packed,
-               plan_row0[tile], plan_rows[tile], q - tile * nt_n};
+               plan_row0[tile], plan_rows[tile], q - tile * nt_n, lora_t,
+               lora_t ? lora_b + (size_t)e * lora_b_stride : nullptr, lora_r};
     const int nrb = (a.nrows + 15) >> 4;
     gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU>(nrb, a, lds, wave, lane);
   }
@@ -401,7 +437,8 @@ template <int MB, int NW, int RG, int S, bool SWIGLU>
 static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int topk,
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                                int packed, int64_t max_items, hipStream_t stream) {
+                                int packed, const LoraArgs& lora, int64_t max_items,
+                                hipStream_t stream) {
   auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU>;
   static int per_cu = 0;  // resident workgroups per CU, fixed per build
   static int cus = 0;
@@ -420,7 +457,8 @@ static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int to
   grid = (grid + 7) / 8 * 8;
   if (grid < 8) grid = 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, stream, A, gather, topk, W,
-                     wstride, C, plan, max_tiles, K, n_out, up_row0, packed);
+                     wstride, C, plan, max_tiles, K, n_out, up_row0, packed, lora.t, lora.b,
+                     lora.b_stride, lora.rank);
   return hipGetLastError();
 }
 
@@ -457,15 +495,16 @@ hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N,
 hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                               int packed, int64_t max_items, hipStream_t stream) {
+                               int packed, const LoraArgs& lora, int64_t max_items,
+                               hipStream_t stream) {
 #define BEAM_STREAM_CASE(MBV, NWV, RGV, SV)                                                     \
   case MBV:                                                                                     \
     return swiglu ? launch_stream<MBV, NWV, RGV, SV, true>(A, gather, topk, W, wstride, C,      \
                                                            plan, max_tiles, K, n_out, up_row0,  \
-                                                           packed, max_items, stream)           \
+                                                           packed, lora, max_items, stream)     \
                   : launch_stream<MBV, NWV, RGV, SV, false>(A, gather, topk, W, wstride, C,     \
                                                             plan, max_tiles, K, n_out, up_row0, \
-                                                            packed, max_items, stream);
+                                                            packed, lora, max_items, stream);
   switch (mb) {
     BEAM_STREAM_CASE(4, 4, 1, BEAM_GEMM_S4)
     BEAM_STREAM_CASE(8, BEAM_GEMM_NW8, BEAM_GEMM_RG8, BEAM_GEMM_S8)

@@ -26,10 +26,21 @@ int ffn_rows_per_tile(int mb);
 int ffn_out_cols_per_item(bool swiglu);
 hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* plan, int max_tiles,
                             hipStream_t stream);
+// Expert LoRA second factor for the bf16 expert GEMMs (t == nullptr: none).
+struct LoraArgs {
+  const uint16_t* t = nullptr;  // [rows, rank] bf16, scaled first factor
+  const uint16_t* b = nullptr;  // [E, n_total, rank] bf16
+  int64_t b_stride = 0;         // elements per expert of b
+  int rank = 0;
+};
 hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
-                               int packed, int64_t max_items, hipStream_t stream);
+                               int packed, const LoraArgs& lora, int64_t max_items,
+                               hipStream_t stream);
+hipError_t launch_lora_a(const uint16_t* X, const int32_t* gather, int topk, const uint16_t* La,
+                         int K, int rank, float scale, uint16_t* t, const int32_t* plan,
+                         int max_tiles, hipStream_t stream);
 hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N, int K,
                                hipStream_t stream);
 

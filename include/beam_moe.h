@@ -62,7 +62,9 @@ enum moe_entry {
   MOE_ENTRY_PERMUTE = 1,
   MOE_ENTRY_EXPERT_FFN = 2,
   MOE_ENTRY_LAYER = 3,
-  MOE_ENTRY_EXPERT_STAGE = 4  /* moe_expert_gate_up or moe_expert_down */
+  MOE_ENTRY_EXPERT_STAGE = 4,  /* moe_expert_gate_up or moe_expert_down */
+  MOE_ENTRY_EXPERT_FFN_LORA = 5,
+  MOE_ENTRY_LAYER_LORA = 6
 };
 
 typedef struct moe_config {
@@ -253,6 +255,41 @@ int moe_layer_forward_fp8(const moe_config_t* cfg, const uint16_t* x, const floa
                           const uint8_t* q_down, const float* s_down, uint16_t* out,
                           int32_t* topk_ids_out, float* topk_w_out,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Expert LoRA ("Beam 1.0" miles recipes, section 5.5 "LoRA": an adapter of
+ * rank 16 and alpha 32 on every routed expert, router frozen).  Each expert's
+ * fused gate/up weight and its down weight carry one adapter; an adapted
+ * weight W [out, in] computes W a + scale * B (A a).  The rank-wide first
+ * factor is rounded once to bf16 after scaling: t = bf16(scale * fp32(a . A^T));
+ * the second factor t . B^T accumulates in fp32 with the base GEMM before the
+ * SwiGLU (gate/up) or the output rounding (down).  The down adapter reads the
+ * bf16 h the base down GEMM reads.
+ */
+typedef struct moe_lora {
+  const uint16_t* a_gate_up;  /* [E, r, H] bf16 row-major  */
+  const uint16_t* b_gate_up;  /* [E, 2I, r] bf16 (rows as in w_gate_up: gate, then up) */
+  const uint16_t* a_down;     /* [E, r, I] bf16            */
+  const uint16_t* b_down;     /* [E, H, r] bf16            */
+  int32_t rank;               /* r in {16, 32, 48, 64}; Beam's recipe uses 16 */
+  float scale;                /* alpha / r; Beam's recipe: 32 / 16 = 2 */
+} moe_lora_t;
+
+/*
+ * moe_expert_ffn and moe_layer_forward with expert LoRA on bf16 base weights
+ * (base weights in cfg->weight_layout; adapters row-major, 16-byte aligned).
+ * Workspace: MOE_ENTRY_EXPERT_FFN_LORA / MOE_ENTRY_LAYER_LORA.  A missing or
+ * malformed `lora` returns MOE_ERR_INVALID_ARG.
+ */
+int moe_expert_ffn_lora(const moe_config_t* cfg, const uint16_t* x, const int32_t* perm_src,
+                        const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
+                        const moe_lora_t* lora, uint16_t* y_perm,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int moe_layer_forward_lora(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                           const float* sel_bias, const uint16_t* w_gate_up,
+                           const uint16_t* w_down, const moe_lora_t* lora, uint16_t* out,
+                           int32_t* topk_ids_out, float* topk_w_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* moe_status_string(int status);

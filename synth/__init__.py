@@ -41,6 +41,7 @@ TAG_DOWN = 3
 TAG_HOT = 4
 TAG_MIX = 5
 TAG_BIAS = 6
+TAG_LORA = 7
 
 
 # ---------------------------------------------------------------------------
@@ -234,6 +235,19 @@ def make_x(w: Workload, seed: int = 0, device="cpu", w_router: torch.Tensor | No
 def make_sel_bias(w: Workload, seed: int = 0, std: float = 0.05, device="cpu") -> torch.Tensor:
     """Optional per-expert selection bias, fp32 [E] (off unless asked for)."""
     return counter_normal(stream_key(seed, TAG_BIAS), w.E, std, device=device)
+
+
+def make_lora(w: Workload, seed: int = 0, device="cpu", rank: int = 16, std: float = 0.02):
+    """Synthetic expert adapters, bf16 and ~N(0, std**2) (nonzero B, unlike a
+    fresh adapter, so that the adapter term is visible): a_gate_up [E, r, H],
+    b_gate_up [E, 2I, r], a_down [E, r, I], b_down [E, H, r]."""
+    shapes = [(w.E, rank, w.H), (w.E, 2 * w.I, rank), (w.E, rank, w.I), (w.E, w.H, rank)]
+    out = []
+    for j, shp in enumerate(shapes):
+        n = shp[0] * shp[1] * shp[2]
+        out.append(counter_normal(stream_key(seed, TAG_LORA, j), n, std, device=device)
+                   .to(torch.bfloat16).view(*shp))
+    return tuple(out)
 
 
 def make_inputs(name: str | Workload, seed: int = 0, device="cpu", experts: bool = True,

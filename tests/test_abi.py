@@ -217,3 +217,36 @@ def test_fp8_binding_checks_dtypes():
     with pytest.raises((ValueError, TypeError)):
         gtr.expert_ffn_fp8(torch.zeros(4, 256, dtype=torch.bfloat16),
                            torch.zeros(32, dtype=torch.int32), torch.zeros(257, dtype=torch.int32), w)
+
+
+def test_lora_entry_points_validate_adapter():
+    lib = gtr.lib()
+    cfg = _cfg()
+    big = 1 << 40
+
+    def lora(**kw):
+        d = dict(a_gate_up=0x10000, b_gate_up=0x20000, a_down=0x30000, b_down=0x40000, rank=16,
+                 scale=2.0)
+        d.update(kw)
+        return L.MoeLora(d["a_gate_up"], d["b_gate_up"], d["a_down"], d["b_down"], d["rank"],
+                         d["scale"])
+
+    def ffn(lo, nb=big, c=cfg):
+        return lib.moe_expert_ffn_lora(ctypes.byref(c), A, A, A, A, A,
+                                       None if lo is None else ctypes.byref(lo), A, A, nb, None)
+
+    assert ffn(None) == L.MOE_ERR_INVALID_ARG
+    for bad in (dict(rank=8), dict(rank=24), dict(rank=128), dict(rank=0),
+                dict(scale=float("nan")), dict(a_down=0), dict(b_gate_up=0x20008)):
+        assert ffn(lora(**bad)) == L.MOE_ERR_INVALID_ARG, bad
+    need = gtr.workspace_bytes(cfg, L.ENTRY_EXPERT_FFN_LORA)
+    assert need > gtr.workspace_bytes(cfg, L.ENTRY_EXPERT_FFN)
+    assert ffn(lora(), nb=need - 1) == L.MOE_ERR_WORKSPACE
+    zero = _cfg(num_tokens=0)
+    assert ffn(lora(), nb=gtr.workspace_bytes(zero, L.ENTRY_EXPERT_FFN_LORA), c=zero) == L.MOE_OK
+    lay = lambda lo, nb: lib.moe_layer_forward_lora(ctypes.byref(cfg), A, A, None, A, A,
+                                                    ctypes.byref(lo), A, None, None, A, nb, None)
+    assert lay(lora(rank=20), big) == L.MOE_ERR_INVALID_ARG
+    assert lay(lora(), gtr.workspace_bytes(cfg, L.ENTRY_LAYER_LORA) - 1) == L.MOE_ERR_WORKSPACE
+    if not __import__("torch").cuda.is_available():
+        assert ffn(lora(rank=64), nb=need) == L.MOE_ERR_HIP

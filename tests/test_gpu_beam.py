@@ -10,7 +10,8 @@ launch configuration the benchmark times:
 * the whole layer on sampled tokens, each computed one by one by the oracle;
 * the same with FP8 per-channel weights, quantised on the device, against the
   oracle's own quantisation of the sampled experts (codes and scales bit-exact,
-  outputs on the oracle's dequantised weights).
+  outputs on the oracle's dequantised weights);
+* the same with rank-16 expert LoRA adapters (scale 32 / 16).
 """
 import numpy as np
 import pytest
@@ -169,4 +170,43 @@ def test_beam_layer_fp8(beam, beam_fp8, name):
         assert_close(to_np(y[r0:r1]), oracle.ffn_rows(xn[rps[r0:r1] // 8], gu, dn),
                      f"y_perm expert {e} rows {r1 - r0}/{rc[e]}")
         acc += rr.weights[t, j] * oracle.ffn_rows(xn[t:t + 1], gu, dn)[0]
+    assert_close(outn[t], 2.5 * acc, f"out token {t}")
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_beam_layer_lora(beam, name):
+    w = synth.workload(name)
+    say(f"[beam:lora:{name}] T={w.T} adapters + layer_forward_lora")
+    ts = synth.make_lora(synth.workload("prefill"), 0, DEV, rank=oracle.LORA_RANK)
+    s = oracle.lora_scale()
+    lw = gtr.LoraWeights(*ts, scale=s)
+    x = synth.make_x(w, 0, DEV, w_router=beam["w_router"])
+    out, ids, wts = gtr.layer_forward_lora(x, beam["w_router"], beam["p_gate_up"],
+                                           beam["p_down"], lw, weight_layout=gtr.LAYOUT_PACKED,
+                                           return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    xn = to_np(x)
+    rr = oracle.route(xn, beam["wr_np"])
+    check_routing(to_np(ids), to_np(wts), rr)
+    rc, ro, rps, rpd = oracle.permute(rr.ids, 256)
+    y = gtr.expert_ffn_lora(x, torch.from_numpy(rps.astype(np.int32)).to(DEV),
+                            torch.from_numpy(ro.astype(np.int32)).to(DEV), beam["w_gate_up"],
+                            beam["w_down"], lw)
+    lora_e = lambda e: tuple(to_np(t[e]) for t in ts)
+    rng = np.random.default_rng(2)
+    cand = np.nonzero(rr.margin >= oracle.MARGIN_TOL)[0]
+    t = int(rng.choice(cand))
+    outn = to_np(out)
+    acc = np.zeros(xn.shape[1])
+    for j, e in enumerate(rr.ids[t]):
+        e = int(e)
+        gu, dn = _expert_np(beam, e)
+        le = lora_e(e)
+        r0, r1 = int(ro[e]), int(ro[e + 1])
+        r1 = min(r1, r0 + 192)
+        if j < 2:  # two experts' rows of the expert MLPs
+            assert_close(to_np(y[r0:r1]), oracle.ffn_rows_lora(xn[rps[r0:r1] // 8], gu, dn, le, s),
+                         f"y_perm expert {e} rows {r1 - r0}/{rc[e]}")
+        acc += rr.weights[t, j] * oracle.ffn_rows_lora(xn[t:t + 1], gu, dn, le, s)[0]
     assert_close(outn[t], 2.5 * acc, f"out token {t}")
