@@ -12,7 +12,7 @@ hidden 5120, intermediate 2560, 256 experts); `roofline` describes the
 dominant kernel (the gate/up grouped GEMM), timed with HIP events on the
 stream it runs on; `decode` reports the weight-streaming T=32 batch in GB/s;
 `fp8` times the same layer with FP8 per-channel expert weights (prefill and
-decode); `cpu_baseline` times the CPU oracle on a bounded sample of the same
+decode); `lora` times it with rank-16 expert LoRA adapters; `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload.
 """
 from __future__ import annotations
@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight variant")
+    p.add_argument("--no-lora", action="store_true", help="skip the expert-LoRA variant")
     p.add_argument("--cpu-experts", type=int, default=256,
                    help="experts whose rows the CPU oracle processes in its timed sample")
     p.add_argument("--no-row-major-ref", action="store_true",
@@ -338,6 +339,39 @@ def main():
                          "stage_ms": {k: round(v, 4) for k, v in f["stage_ms"].items()}}
             del f
         result["fp8"] = fp8
+    if not args.no_lora:
+        # rank-16 expert LoRA (scale 32 / 16) on the packed bf16 experts
+        print("[bench] timing expert LoRA (rank 16)", file=sys.stderr, flush=True)
+        ad = synth.make_lora(beam, args.seed, dev, rank=16)
+        lw = gtr.LoraWeights(*ad, scale=2.0)
+        lo = {"rank": 16, "scale": 2.0, "adapter_bytes": sum(t.numel() * 2 for t in ad)}
+        for name in ([args.workload] + ([] if args.no_decode or args.workload == "decode"
+                                        else ["decode"])):
+            wl = synth.workload(name)
+            xl = synth.make_x(wl, args.seed, dev, w_router=wts["w_router"])
+            ws = gtr.Workspace()
+            call = lambda: gtr.layer_forward_lora(xl, wts["w_router"], wts["p_gate_up"],
+                                                  wts["p_down"], lw,
+                                                  weight_layout=gtr.LAYOUT_PACKED, workspace=ws)
+            base = lambda: gtr.layer_forward(xl, wts["w_router"], wts["p_gate_up"],
+                                             wts["p_down"], weight_layout=gtr.LAYOUT_PACKED,
+                                             workspace=ws)
+            n = args.steps if name == args.workload else max(args.steps, 10)
+            res = {}
+            for tag, fn in (("lora", call), ("base", base)):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                for _ in range(n):
+                    fn()
+                torch.cuda.synchronize()
+                res[tag] = (time.perf_counter() - t1) * 1e3 / n
+            lo[name] = {"tokens": wl.T, "layer_forward_ms": round(res["lora"], 4),
+                        "tokens_per_s": round(wl.T / (res["lora"] * 1e-3), 1),
+                        "overhead_vs_bf16_layer": round(res["lora"] / res["base"] - 1.0, 4)}
+        result["lora"] = lo
+        del ad, lw
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, r["x"], wts, args.cpu_experts, torch)
