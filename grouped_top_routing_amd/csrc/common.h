@@ -114,4 +114,20 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
       : "memory");
 }
 
+// As lds_dma16, with the non-temporal cache policy: for data read once (the
+// expert weight streams), so it does not displace reused lines in the caches.
+__device__ __forceinline__ void lds_dma16_nt(const void* g, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_addr)
+      : "memory");
+}
+
 }  // namespace beam

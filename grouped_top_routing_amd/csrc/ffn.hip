@@ -115,6 +115,12 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
   constexpr int WCOLS = CG * HALF * 16;
   constexpr int RBX = RB > 0 ? RB : 1;
+  // Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
+  // weight stream: weights are then loaded with the non-temporal policy,
+  // which measured 6.6 TB/s against 6.1 TB/s with the default one.  The
+  // 192-row configuration keeps the default (it was 1-20 % slower with
+  // non-temporal loads, most at the skewed batch that re-reads hot experts).
+  constexpr bool kStreamWeights = MB <= 8;
   static_assert(CG * RG == kNW && NCBW * CG == kItemBlocks && NBL * RG == NCBW, "work split");
   // A fragments this wave loads: blocks wave, wave + kNW, ... below NRB
   constexpr int AMAX = (NRB + kNW - 1) / kNW;
@@ -163,8 +169,12 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     const uint32_t so = (uint32_t)((st % S) * SLOT);
     const int k0 = st * kBKS;
 #pragma unroll
-    for (int t = 0; t < NBL; ++t)
-      lds_dma16(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
+    for (int t = 0; t < NBL; ++t) {
+      if constexpr (kStreamWeights)
+        lds_dma16_nt(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
+      else
+        lds_dma16(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
+    }
 #pragma unroll
     for (int j = 0; j < AMAX; ++j)
       if (j < na) lds_dma16(asrc[j] + k0, a_base + so + kNW * j * kFrag);

@@ -152,8 +152,12 @@ __device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
   auto issue = [&](int st) {
     const uint32_t so = (uint32_t)((st % S) * SLOT);
 #pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb)
-      lds_dma16(bsrc[cb] + (size_t)st * kFragB, b_base + so + cb * kFragB);
+    for (int cb = 0; cb < NCBW; ++cb) {
+      if constexpr (MB <= 8)  // weight streams read once: non-temporal (as in ffn.hip)
+        lds_dma16_nt(bsrc[cb] + (size_t)st * kFragB, b_base + so + cb * kFragB);
+      else
+        lds_dma16(bsrc[cb] + (size_t)st * kFragB, b_base + so + cb * kFragB);
+    }
 #pragma unroll
     for (int j = 0; j < AMAX; ++j)
       if (j < na) {

@@ -50,13 +50,17 @@ __global__ __launch_bounds__(256) void lora_a_kernel(const uint16_t* __restrict_
     f32x4_t acc[RB];
 #pragma unroll
     for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < K; k += kK) {
-      const bf16x8_t a = as_bf16x8(ld16(ap + k));
+    // K is a multiple of 128 (hidden % 256 == 0, intermediate % 128 == 0)
+    for (int k0 = 0; k0 < K; k0 += 4 * kK) {
 #pragma unroll
-      for (int j = 0; j < RB; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a, as_bf16x8(ld16(bp + (size_t)j * 16 * K + k)), acc[j], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * kK;
+        const bf16x8_t a = as_bf16x8(ld16(ap + k));
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, as_bf16x8(ld16(bp + (size_t)j * 16 * K + k)), acc[j], 0, 0, 0);
+      }
     }
     // lane holds rows 4g..4g+3 of rank column j*16 + r
 #pragma unroll
