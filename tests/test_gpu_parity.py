@@ -140,12 +140,12 @@ def test_expert_ffn(tiny):
 
 
 @pytest.mark.parametrize("hot_rows,T", [(1, 64), (17, 64), (40, 200), (130, 700), (300, 1024),
-                                        (1000, 2048)])
+                                        (1000, 2048), (700, 3072), (2500, 4096)])
 def test_expert_ffn_ragged_tiles(tiny, hot_rows, T):
     # one expert gets `hot_rows` rows, the rest spread thinly: m-tiles with
     # ragged tails, experts with a single row, and every m-tile height the
-    # library picks from the mean rows per expert (T=64 -> 16 rows, 200/700 ->
-    # 32, 1024 -> 64, 2048 -> 128)
+    # library picks from the mean rows per expert (up to 1024 tokens -> 64-row
+    # tiles, 2048 -> 128, 3072 and 4096 -> 192)
     say(f"[expert_ffn] ragged hot_rows={hot_rows} T={T}")
     npd = tiny["np"]
     rng = np.random.default_rng(hot_rows)
