@@ -276,3 +276,44 @@ def test_packed_layout_matches_row_major_bitwise(tiny, T):
     a = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
     b = gtr.layer_forward(x, tiny["w_router"], pgu, pd, weight_layout=gtr.LAYOUT_PACKED)
     assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------- hip graphs
+@pytest.mark.parametrize("variant", ["bf16", "fp8", "lora"])
+def test_layer_replays_from_a_captured_graph(tiny, variant):
+    # every launch of a layer call goes on the caller's stream with no host
+    # synchronisation or allocation inside the library, so the call can be
+    # captured into a HIP graph once and replayed on new inputs
+    say(f"[graph] {variant}")
+    ws = gtr.Workspace()
+    wr, wgu, wd = tiny["w_router"], tiny["w_gate_up"], tiny["w_down"]
+    f8 = gtr.quantize_fp8(wgu, wd) if variant == "fp8" else None
+    lw = (gtr.LoraWeights(*synth.make_lora(tiny["workload"], 0, DEV), scale=2.0)
+          if variant == "lora" else None)
+
+    def call(x):
+        if variant == "fp8":
+            return gtr.layer_forward_fp8(x, wr, f8, workspace=ws)
+        if variant == "lora":
+            return gtr.layer_forward_lora(x, wr, wgu, wd, lw, workspace=ws)
+        return gtr.layer_forward(x, wr, wgu, wd, workspace=ws)
+
+    static_x = tiny["x"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(static_x)  # warm-up: workspace sized, launch shapes cached
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        static_out = call(static_x)
+    for rep in range(3):
+        x = synth.make_x(synth.workload("tiny"), 100 + rep, DEV)
+        static_x.copy_(x)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = static_out.clone()
+        want = call(x)          # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"replay {rep} differs from the eager call"
