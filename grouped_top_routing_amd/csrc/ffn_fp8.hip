@@ -106,20 +106,33 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-template <int NRB, int MB, int NW, int NCBW, int S, bool SWIGLU>
-__device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
-                                         const int32_t* __restrict__ gather, int topk,
-                                         const uint8_t* __restrict__ Qe,
-                                         const float* __restrict__ Se, uint16_t* __restrict__ C,
-                                         int K, int n_out, int up_row0, int row0, int nrows,
-                                         int ntile, uint8_t* lds, int wave, int lane) {
+// The waves form RG row groups x NW / RG column groups over the item's 16
+// weight-row blocks (as in ffn.hip): a wave computes RB of the NRB row blocks
+// (from block row_off) for NCBW column blocks and loads NCBW / RG of those
+// blocks' weight fragments.
+constexpr int kItemBlocks = 16;
+
+template <int NRB, int RB, int MB, int NW, int RG, int S, bool SWIGLU>
+__device__ __forceinline__ void fp8_item_rows(const uint16_t* __restrict__ A,
+                                              const int32_t* __restrict__ gather, int topk,
+                                              const uint8_t* __restrict__ Qe,
+                                              const float* __restrict__ Se,
+                                              uint16_t* __restrict__ C, int K, int n_out,
+                                              int up_row0, int row0, int nrows, int ntile,
+                                              uint8_t* lds, int wave, int lane, int row_off) {
+  constexpr int CG = NW / RG;
+  constexpr int NCBW = kItemBlocks / CG;
+  constexpr int NBL = NCBW / RG;
   constexpr int D = S - 1;
-  constexpr int AOFF = NW * NCBW * kFragB;        // slot = B fragments, then A (2 per block)
+  constexpr int AOFF = kItemBlocks * kFragB;      // slot = B fragments, then A (2 per block)
   constexpr int SLOT = AOFF + 2 * MB * kFragB;
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
-  constexpr int WCOLS = NW * HALF * 16;
+  constexpr int WCOLS = CG * HALF * 16;
   constexpr int AMAX = (NRB + NW - 1) / NW;
+  constexpr int RBX = RB > 0 ? RB : 1;
+  static_assert(CG * RG == NW && NCBW * CG == kItemBlocks && NBL * RG == NCBW, "work split");
   const int r = lane & 15, g = lane >> 4;
+  const int cg = wave % CG, rg = wave / CG;
   const int nk = K / kStageK;
   const int na = (NRB - wave + NW - 1) / NW;      // A row blocks this wave loads
 
@@ -131,32 +144,34 @@ __device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
     const int src = gather ? gather[row0 + row] / topk : row0 + row;
     asrc[j] = A + (size_t)src * K + 8 * g;
   }
-  const uint8_t* bsrc[NCBW];
-  float scale[NCBW];
-#pragma unroll
-  for (int cb = 0; cb < NCBW; ++cb) {
-    int wrow;
+  auto weight_row = [&](int cb) {
     if (SWIGLU) {
       const int j = cb % HALF;
-      wrow = ntile * WCOLS + wave * HALF * 16 + j * 16 + r + (cb >= HALF ? up_row0 : 0);
-    } else {
-      wrow = ntile * WCOLS + wave * NCBW * 16 + cb * 16 + r;
+      return ntile * WCOLS + cg * HALF * 16 + j * 16 + r + (cb >= HALF ? up_row0 : 0);
     }
-    bsrc[cb] = Qe + (size_t)((wrow - r) >> 4) * nk * kFragB + lane * 16;
-    scale[cb] = Se[wrow];
+    return ntile * WCOLS + cg * NCBW * 16 + cb * 16 + r;
+  };
+  const uint8_t* bsrc[NBL];
+#pragma unroll
+  for (int t = 0; t < NBL; ++t) {
+    const int wrow = weight_row(rg + RG * t);
+    bsrc[t] = Qe + (size_t)((wrow - r) >> 4) * nk * kFragB + lane * 16;
   }
+  float scale[NCBW];
+#pragma unroll
+  for (int cb = 0; cb < NCBW; ++cb) scale[cb] = Se[weight_row(cb)];
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
-  const uint32_t b_base = lds0 + wave * NCBW * kFragB;
+  const uint32_t b_base = lds0 + (cg * NCBW + rg) * kFragB;
   const uint32_t a_base = lds0 + AOFF + wave * 2 * kFragB;
 
   auto issue = [&](int st) {
     const uint32_t so = (uint32_t)((st % S) * SLOT);
 #pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb) {
+    for (int t = 0; t < NBL; ++t) {
       if constexpr (MB <= 8)  // weight streams read once: non-temporal (as in ffn.hip)
-        lds_dma16_nt(bsrc[cb] + (size_t)st * kFragB, b_base + so + cb * kFragB);
+        lds_dma16_nt(bsrc[t] + (size_t)st * kFragB, b_base + so + RG * t * kFragB);
       else
-        lds_dma16(bsrc[cb] + (size_t)st * kFragB, b_base + so + cb * kFragB);
+        lds_dma16(bsrc[t] + (size_t)st * kFragB, b_base + so + RG * t * kFragB);
     }
 #pragma unroll
     for (int j = 0; j < AMAX; ++j)
@@ -167,9 +182,9 @@ __device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
       }
   };
 
-  f32x4_t acc[NRB][NCBW];
+  f32x4_t acc[RBX][NCBW];
 #pragma unroll
-  for (int i = 0; i < NRB; ++i)
+  for (int i = 0; i < RBX; ++i)
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -179,35 +194,40 @@ __device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
 
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = min(D - 1, nk - 1 - kt);
-    if (na == AMAX) wait_stage<D - 1, NCBW + 2 * AMAX>(ahead);
-    else wait_stage<D - 1, NCBW + 2 * (AMAX > 0 ? AMAX - 1 : 0)>(ahead);
+    if (na == AMAX) wait_stage<D - 1, NBL + 2 * AMAX>(ahead);
+    else wait_stage<D - 1, NBL + 2 * (AMAX > 0 ? AMAX - 1 : 0)>(ahead);
     stage_barrier();  // stage kt visible to all waves; slot (kt - 1) % S is free
     if (kt + D < nk) issue(kt + D);
-    const uint8_t* sl = lds + (kt % S) * SLOT;
-    bf16x8_t blo[NCBW], bhi[NCBW];
+    if constexpr (RB > 0) {
+      const uint8_t* sl = lds + (kt % S) * SLOT;
+      bf16x8_t blo[NCBW], bhi[NCBW];
 #pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(sl + (wave * NCBW + cb) * kFragB + 16 * lane);
-      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-      uint32_t o[8];
+      for (int cb = 0; cb < NCBW; ++cb) {
+        const uint4 raw =
+            *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFragB + 16 * lane);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t o[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[i], 1.0f, false));
-        o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[i], 1.0f, true));
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[i], 1.0f, false));
+          o[2 * i + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[i], 1.0f, true));
+        }
+        blo[cb] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+        bhi[cb] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
       }
-      blo[cb] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
-      bhi[cb] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
-    }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int i = 0; i < NRB; ++i) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
-            sl + AOFF + (2 * i + h) * kFragB + 16 * lane));
+        for (int i = 0; i < RB; ++i) {
+          const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
+              sl + AOFF + (2 * (row_off + i) + h) * kFragB + 16 * lane));
 #pragma unroll
-        for (int cb = 0; cb < NCBW; ++cb)
-          acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h ? bhi[cb] : blo[cb], acc[i][cb],
-                                                               0, 0, 0);
+          for (int cb = 0; cb < NCBW; ++cb)
+            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h ? bhi[cb] : blo[cb],
+                                                                 acc[i][cb], 0, 0, 0);
+        }
       }
     }
   }
@@ -218,25 +238,27 @@ __device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
   constexpr int TSTRIDE = WCOLS + 8;
   static_assert(16 * NRB * TSTRIDE * 2 <= S * SLOT, "epilogue tile fits the ring");
   uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
+  if constexpr (RB > 0) {
 #pragma unroll
-  for (int i = 0; i < NRB; ++i) {
+    for (int i = 0; i < RB; ++i) {
 #pragma unroll
-    for (int j = 0; j < HALF; ++j) {
-      const int col = wave * HALF * 16 + j * 16 + r;
+      for (int j = 0; j < HALF; ++j) {
+        const int col = cg * HALF * 16 + j * 16 + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = i * 16 + 4 * g + v;
-        float o;
-        if (SWIGLU) {
-          const float gt = acc[i][j][v] * scale[j], up = acc[i][j + HALF][v] * scale[j + HALF];
-          o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
-        } else {
-          o = acc[i][j][v] * scale[j];
+        for (int v = 0; v < 4; ++v) {
+          const int row = (row_off + i) * 16 + 4 * g + v;
+          float o;
+          if (SWIGLU) {
+            const float gt = acc[i][j][v] * scale[j], up = acc[i][j + HALF][v] * scale[j + HALF];
+            o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+          } else {
+            o = acc[i][j][v] * scale[j];
+          }
+          const uint32_t bb = f32_to_bf16(o);
+          const uint32_t nb = __shfl_xor(bb, 1);
+          if ((r & 1) == 0)
+            *reinterpret_cast<uint32_t*>(tile + row * TSTRIDE + col) = bb | (nb << 16);
         }
-        const uint32_t bb = f32_to_bf16(o);
-        const uint32_t nb = __shfl_xor(bb, 1);
-        if ((r & 1) == 0)
-          *reinterpret_cast<uint32_t*>(tile + row * TSTRIDE + col) = bb | (nb << 16);
       }
     }
   }
@@ -254,7 +276,29 @@ __device__ __forceinline__ void fp8_item(const uint16_t* __restrict__ A,
   stage_barrier();
 }
 
-template <int N, int MB, int NW, int NCBW, int S, bool SWIGLU>
+template <int NRB, int MB, int NW, int RG, int S, bool SWIGLU>
+__device__ __forceinline__ void fp8_item(const uint16_t* A, const int32_t* gather, int topk,
+                                         const uint8_t* Qe, const float* Se, uint16_t* C, int K,
+                                         int n_out, int up_row0, int row0, int nrows, int ntile,
+                                         uint8_t* lds, int wave, int lane) {
+  if constexpr (RG == 1) {
+    fp8_item_rows<NRB, NRB, MB, NW, 1, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out, up_row0,
+                                                  row0, nrows, ntile, lds, wave, lane, 0);
+  } else {
+    static_assert(RG == 2, "one or two row groups");
+    constexpr int RB0 = (NRB + 1) / 2;
+    if (wave < NW / 2)
+      fp8_item_rows<NRB, RB0, MB, NW, 2, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out,
+                                                    up_row0, row0, nrows, ntile, lds, wave, lane,
+                                                    0);
+    else
+      fp8_item_rows<NRB, NRB - RB0, MB, NW, 2, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out,
+                                                          up_row0, row0, nrows, ntile, lds, wave,
+                                                          lane, RB0);
+  }
+}
+
+template <int N, int MB, int NW, int RG, int S, bool SWIGLU>
 __device__ __forceinline__ void fp8_dispatch(int nrb, const uint16_t* A, const int32_t* gather,
                                              int topk, const uint8_t* Qe, const float* Se,
                                              uint16_t* C, int K, int n_out, int up_row0, int row0,
@@ -264,22 +308,22 @@ __device__ __forceinline__ void fp8_dispatch(int nrb, const uint16_t* A, const i
     return;
   } else {
     if (nrb == N)
-      fp8_item<N, MB, NW, NCBW, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out, up_row0, row0,
-                                           nrows, ntile, lds, wave, lane);
+      fp8_item<N, MB, NW, RG, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out, up_row0, row0,
+                                         nrows, ntile, lds, wave, lane);
     else
-      fp8_dispatch<N + 1, MB, NW, NCBW, S, SWIGLU>(nrb, A, gather, topk, Qe, Se, C, K, n_out,
-                                                   up_row0, row0, nrows, ntile, lds, wave, lane);
+      fp8_dispatch<N + 1, MB, NW, RG, S, SWIGLU>(nrb, A, gather, topk, Qe, Se, C, K, n_out,
+                                                 up_row0, row0, nrows, ntile, lds, wave, lane);
   }
 }
 
-template <int MB, int NW, int NCBW, int S, bool SWIGLU>
+template <int MB, int NW, int RG, int S, bool SWIGLU>
 __global__ __launch_bounds__(NW * 64, 1) void stream_gemm_fp8_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint8_t* __restrict__ Q, const float* __restrict__ scales, int64_t q_expert_stride,
     int N, uint16_t* __restrict__ C, const int32_t* __restrict__ plan, int max_tiles, int K,
     int n_out, int up_row0) {
-  constexpr int SLOT = (NW * NCBW + 2 * MB) * kFragB;
-  constexpr int WCOLS = NW * (SWIGLU ? NCBW / 2 : NCBW) * 16;
+  constexpr int SLOT = (kItemBlocks + 2 * MB) * kFragB;
+  constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? 128 : 256), "item width matches the bf16 kernels");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S * SLOT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -296,19 +340,19 @@ __global__ __launch_bounds__(NW * 64, 1) void stream_gemm_fp8_kernel(
     if (q >= total) break;
     const int tile = q / nt_n;
     const int e = plan_expert[tile], row0 = plan_row0[tile], nrows = plan_rows[tile];
-    fp8_dispatch<1, MB, NW, NCBW, S, SWIGLU>((nrows + 15) >> 4, A, gather, topk,
+    fp8_dispatch<1, MB, NW, RG, S, SWIGLU>((nrows + 15) >> 4, A, gather, topk,
                                              Q + (size_t)e * q_expert_stride,
                                              scales + (size_t)e * N, C, K, n_out, up_row0, row0,
                                              nrows, q - tile * nt_n, lds, wave, lane);
   }
 }
 
-template <int MB, int NW, int NCBW, int S, bool SWIGLU>
+template <int MB, int NW, int RG, int S, bool SWIGLU>
 static hipError_t launch_fp8(const uint16_t* A, const int32_t* gather, int topk, const uint8_t* Q,
                              const float* scales, int64_t qstride, int N, uint16_t* C,
                              const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                              int64_t max_items, hipStream_t stream) {
-  auto kern = stream_gemm_fp8_kernel<MB, NW, NCBW, S, SWIGLU>;
+  auto kern = stream_gemm_fp8_kernel<MB, NW, RG, S, SWIGLU>;
   static int per_cu = 0, cus = 0;
   if (per_cu == 0) {
     int dev = 0, n = 0, occ = 0;
@@ -338,15 +382,15 @@ int ffn_fp8_choose_mb(int64_t rows, int E) {
   return 12;
 }
 
-// Pipeline shapes (waves, stages) of the 128- and 192-row configurations.
-#ifndef BEAM_FP8_NW8
-#define BEAM_FP8_NW8 8
+// Pipeline shapes (row groups, stages) of the 128- and 192-row configurations.
+#ifndef BEAM_FP8_RG8
+#define BEAM_FP8_RG8 2
 #endif
 #ifndef BEAM_FP8_S8
 #define BEAM_FP8_S8 3
 #endif
-#ifndef BEAM_FP8_NW12
-#define BEAM_FP8_NW12 8
+#ifndef BEAM_FP8_RG12
+#define BEAM_FP8_RG12 2
 #endif
 #ifndef BEAM_FP8_S12
 #define BEAM_FP8_S12 3
@@ -356,18 +400,18 @@ hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const
                                    int topk, const uint8_t* Q, const float* scales, int64_t qstride,
                                    int N, uint16_t* C, const int32_t* plan, int max_tiles, int K,
                                    int n_out, int up_row0, int64_t max_items, hipStream_t stream) {
-#define BEAM_FP8_CASE(MBV, NWV, NCBWV, SV)                                                      \
+#define BEAM_FP8_CASE(MBV, NWV, RGV, SV)                                                      \
   case MBV:                                                                                     \
-    return swiglu ? launch_fp8<MBV, NWV, NCBWV, SV, true>(A, gather, topk, Q, scales, qstride,  \
+    return swiglu ? launch_fp8<MBV, NWV, RGV, SV, true>(A, gather, topk, Q, scales, qstride,  \
                                                           N, C, plan, max_tiles, K, n_out,      \
                                                           up_row0, max_items, stream)           \
-                  : launch_fp8<MBV, NWV, NCBWV, SV, false>(A, gather, topk, Q, scales, qstride, \
+                  : launch_fp8<MBV, NWV, RGV, SV, false>(A, gather, topk, Q, scales, qstride, \
                                                            N, C, plan, max_tiles, K, n_out,     \
                                                            up_row0, max_items, stream);
   switch (mb) {
-    BEAM_FP8_CASE(2, 4, 4, 4)
-    BEAM_FP8_CASE(8, BEAM_FP8_NW8, 16 / BEAM_FP8_NW8, BEAM_FP8_S8)
-    BEAM_FP8_CASE(12, BEAM_FP8_NW12, 16 / BEAM_FP8_NW12, BEAM_FP8_S12)
+    BEAM_FP8_CASE(2, 4, 1, 4)
+    BEAM_FP8_CASE(8, 8, BEAM_FP8_RG8, BEAM_FP8_S8)
+    BEAM_FP8_CASE(12, 8, BEAM_FP8_RG12, BEAM_FP8_S12)
     default:
       return hipErrorInvalidValue;
   }
