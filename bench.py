@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight variant")
     p.add_argument("--no-lora", action="store_true", help="skip the expert-LoRA variant")
+    p.add_argument("--no-attainable", action="store_true",
+                   help="skip the torch copy / matmul reference points")
     p.add_argument("--cpu-experts", type=int, default=256,
                    help="experts whose rows the CPU oracle processes in its timed sample")
     p.add_argument("--no-row-major-ref", action="store_true",
@@ -152,6 +154,9 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16"):
     names = ["route", "permute", "gate_up", "down", "combine"]
     stage = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
              for j, n in enumerate(names)}
+    # device time of each step (first to last event of the step)
+    per_step = sorted(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps))
+    pct = lambda q: per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
     # the single-call entry point, for reference, in both weight layouts
     def time_layer(a, b, layout):
         for _ in range(2):
@@ -176,6 +181,7 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16"):
         rowmajor_ms = (None if args.no_row_major_ref else
                        time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
+            "device_step_ms": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
             "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
             "counts": counts.cpu().numpy(), "ids": ids}
 
@@ -289,6 +295,8 @@ def main():
                      "traffic": measured_traffic() if w.name == "prefill" else None,
                      "bytes_per_launch": alg["gate_up_bytes"], "avg_launch_ms": round(gu_ms, 4)},
         "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "roofline_frac": round(max(layer_gbs / HBM_PEAK_GBS, mfma_frac), 4),
+                  "device_step_ms": {k: round(v, 4) for k, v in r["device_step_ms"].items()},
                   "bf16_mfma_frac": round(mfma_frac, 4), "algorithmic_bytes": alg["layer_bytes"],
                   "expert_flops": alg["expert_flops"], "touched_experts": alg["touched"],
                   "layer_forward_ms": round(r["layer_forward_ms"], 4),
@@ -300,6 +308,31 @@ def main():
                                 "lt10": int((c < 10).sum()), "empty": int((c == 0).sum())}},
         "git": git_sha(),
     }
+    if not args.no_attainable:
+        # reference points measured with torch's own kernels (not this library):
+        # a device-to-device copy and a large bf16 matmul
+        a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        m = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        for _ in range(2):
+            b.copy_(a)
+            torch.matmul(m, m)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        for _ in range(5):
+            b.copy_(a)
+        e[1].record()
+        for _ in range(5):
+            torch.matmul(m, m)
+        e[2].record()
+        torch.cuda.synchronize()
+        copy_ms = e[0].elapsed_time(e[1]) / 5
+        mm_ms = e[1].elapsed_time(e[2]) / 5
+        result["attainable_reference"] = {
+            "torch_copy_gbs_read_plus_write": round(2 * a.numel() / (copy_ms * 1e-3) / 1e9, 1),
+            "torch_bf16_matmul_8192_tflops": round(2 * 8192 ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+        del a, b, m
     if not args.no_decode and args.workload != "decode":
         print("[bench] timing decode T=32", file=sys.stderr, flush=True)
         d = run_workload("decode", wts, args, max(args.steps, 10), 3, gtr, synth, torch)

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (rows[j] >= 0) {
-        const uint4 q = ld16(y + (size_t)rows[j] * H + 8 * v);
+        const uint4 q = ld16_nt(y + (size_t)rows[j] * H + 8 * v);  // each y row is read once
         const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {

@@ -30,6 +30,12 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
+// 16-byte global load with the non-temporal cache policy (data read once).
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8_t, v);
