@@ -20,10 +20,12 @@
 //   through an S-stage ring.  S-1 stages of 32 k are always in flight; each
 //   wave waits on its own vmcnt and one s_barrier per stage publishes the
 //   stage to the other waves.
-// * One 1 KB "fragment" is exactly one MFMA operand (16 rows x 32 k, bf16):
-//   lane l fetches row l%16, k chunk (l/16)*8, and later reads the same 16
-//   bytes back with a conflict-free ds_read_b128 at lane*16.  Every operand
-//   is loaded and read in the v_mfma_f32_16x16x32_bf16 lane order, so A and B
+// * One 1 KB weight "fragment" is exactly one MFMA operand (16 rows x 32 k,
+//   bf16): lane l fetches row l%16, k chunk (l/16)*8, and later reads the
+//   same 16 bytes back with a conflict-free ds_read_b128 at lane*16.  The
+//   gathered A rows are staged the same way for 64-row tiles, and 64 k at a
+//   time in whole 128-byte lines for larger tiles (layout below).  Every
+//   operand is read in the v_mfma_f32_16x16x32_bf16 lane order, so A and B
 //   lanes always carry matching k.
 // * A work item is one (m-tile, n-tile) pair.  A device-built plan cuts each
 //   expert's rows into balanced m-tiles of at most 16*MB rows, so at Beam's
@@ -100,6 +102,27 @@ struct ItemArgs {
 // every A fragment).
 constexpr int kItemBlocks = 16;
 
+// LDS ring layouts.  64-row tiles: S slots of [16 B fragments | MB A
+// fragments], every A fragment a 16-row x 32-k MFMA operand (64 bytes of 16
+// rows).  128/192-row tiles stage A 64 k at a time, a "pair" of 32-k stages,
+// so that every A load fetches whole 128-byte lines (the half-line loads cost
+// ~10% at prefill): per 16-row block a pair holds 2 KB, rows 0-7 then rows
+// 8-15, each row's 128 bytes with its 16-byte chunks XOR-swizzled by
+// (row / 2) % 8 so that the MFMA operand reads (16 rows at one logical chunk)
+// hit distinct LDS banks.  B then has its own ring of S 16 KB slots and A a
+// ring of Q pair slots, Q a power of two with 2Q >= S + 1: a pair is refilled
+// only after both of its stages were read and waited for by every wave.
+template <int MB>
+constexpr bool pair_a() { return MB >= 8; }
+template <int S>
+constexpr int pair_slots() { return (S + 2) / 2 <= 2 ? 2 : ((S + 2) / 2 <= 4 ? 4 : 8); }
+__device__ __forceinline__ int a_swizzle(int row) { return (row >> 1) & 7; }
+template <int MB, int S>
+constexpr int ring_bytes() {
+  return pair_a<MB>() ? S * kItemBlocks * kFrag + pair_slots<S>() * MB * 2 * kFrag
+                      : S * (kItemBlocks + MB) * kFrag;
+}
+
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
 // this wave computes RB blocks starting at block row_off.  MB sizes the LDS
 // ring; fragments of blocks NRB..MB-1 are not loaded.
@@ -110,8 +133,13 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int NCBW = kItemBlocks / CG;        // column blocks this wave computes
   constexpr int NBL = NCBW / RG;                // ... and loads per stage (shared with its row peers)
   constexpr int D = S - 1;                      // stages in flight ahead of compute
-  constexpr int AOFF = kItemBlocks * kFrag;     // slot = B fragments, then A fragments
-  constexpr int SLOT = AOFF + MB * kFrag;
+  constexpr bool kPairA = pair_a<MB>();
+  constexpr int AOFF = kItemBlocks * kFrag;     // unpaired slot = B fragments, then A fragments
+  constexpr int SLOT = kPairA ? kItemBlocks * kFrag : AOFF + MB * kFrag;  // B stride per stage
+  constexpr int Q = pair_slots<S>();
+  constexpr int APAIR = MB * 2 * kFrag;         // one A pair slot
+  constexpr int APOFF = S * kItemBlocks * kFrag;
+  static_assert(!kPairA || 2 * Q >= S + 1, "a pair slot outlives the stages reading it");
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
   constexpr int WCOLS = CG * HALF * 16;
   constexpr int RBX = RB > 0 ? RB : 1;
@@ -132,14 +160,27 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // na in {AMAX - 1, AMAX}.  Both values are handled by separate waits.
   const int na = (NRB - wave + kNW - 1) / kNW;
 
-  const uint16_t* asrc[AMAX > 0 ? AMAX : 1];
+  // A sources.  Unpaired: lane = (row r, k chunk g) of a 16 x 32 fragment.
+  // Paired: per 16-row block two loads (hf = rows 0-7, rows 8-15); lane l
+  // fetches row 8 hf + l / 8, the 16-byte chunk that the swizzle places at
+  // position l % 8 of that row's 128 bytes.  Rows are kept as 32-bit indices
+  // (the 192-row configuration has no registers to spare).
+  constexpr int NHF = kPairA ? 2 : 1;
+  int asrow[AMAX > 0 ? AMAX : 1][NHF];
 #pragma unroll
   for (int j = 0; j < AMAX; ++j) {
-    int row = (wave + kNW * j) * 16 + r;
-    row = row < a.nrows ? row : a.nrows - 1;  // rows past the tile repeat its last row
-    const int src = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
-    asrc[j] = a.A + (size_t)src * a.K + 8 * g;
+#pragma unroll
+    for (int hf = 0; hf < NHF; ++hf) {
+      const int rho = kPairA ? hf * 8 + (lane >> 3) : r;
+      int row = (wave + kNW * j) * 16 + rho;
+      row = row < a.nrows ? row : a.nrows - 1;  // rows past the tile repeat its last row
+      asrow[j][hf] = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
+    }
   }
+  auto asrc = [&](int j, int hf, int k0) {
+    const int rho = hf * 8 + (lane >> 3);
+    return a.A + (size_t)asrow[j][hf] * a.K + k0 + 8 * (kPairA ? ((lane & 7) ^ a_swizzle(rho)) : g);
+  };
   // the weight row (output column) of lane r in column block cb of group cg
   auto weight_row = [&](int cb) {
     if (SWIGLU) {
@@ -163,7 +204,12 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
   const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds0 + (cg * NCBW + rg) * kFrag);
-  const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds0 + AOFF + wave * kFrag);
+  const uint32_t a_base = __builtin_amdgcn_readfirstlane(
+      kPairA ? lds0 + APOFF + wave * 2 * kFrag : lds0 + AOFF + wave * kFrag);
+  // byte offset, inside a pair's 2 KB row block, of this lane's MFMA operand
+  // (row r, logical chunk g) for the pair's first stage; the second stage
+  // reads logical chunk 4 + g, the same address with bit 6 flipped
+  const int aoff0 = (r >> 3) * kFrag + (r & 7) * 128 + ((g ^ a_swizzle(r)) << 4);
 
   auto issue = [&](int st) {
     const uint32_t so = (uint32_t)((st % S) * SLOT);
@@ -175,9 +221,22 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       else
         lds_dma16(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
     }
+    if constexpr (kPairA) {
+      if ((st & 1) == 0) {  // the pair (st, st + 1): 64 k of each A row
+        const uint32_t po = (uint32_t)(((st >> 1) % Q) * APAIR);
 #pragma unroll
-    for (int j = 0; j < AMAX; ++j)
-      if (j < na) lds_dma16(asrc[j] + k0, a_base + so + kNW * j * kFrag);
+        for (int j = 0; j < AMAX; ++j)
+          if (j < na) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+              lds_dma16(asrc(j, hf, k0), a_base + po + kNW * j * 2 * kFrag + hf * kFrag);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < AMAX; ++j)
+        if (j < na) lds_dma16(asrc(j, 0, k0), a_base + so + kNW * j * kFrag);
+    }
   };
 
   f32x4_t acc[RBX][NCBW];
@@ -194,51 +253,69 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // min(st + D - 1, nk - 1) have been issued
   auto wait_for = [&](int st) {
     const int ahead = min(D - 1, nk - 1 - st);
-    if (na == AMAX) wait_stage<D - 1, NBL + AMAX>(ahead);
-    else wait_stage<D - 1, NBL + AMAX - 1>(ahead);
+    if constexpr (kPairA) {
+      // later stages carry NBL loads each, even ones 2 na more (their pair)
+      const int evens = ((st + ahead) >> 1) - (st >> 1);
+      wait_vm_dyn<0, 15>(ahead * NBL + evens * 2 * na);
+    } else {
+      if (na == AMAX) wait_stage<D - 1, NBL + AMAX>(ahead);
+      else wait_stage<D - 1, NBL + AMAX - 1>(ahead);
+    }
   };
-  auto read_frags = [&](int st, uint4 (&af)[RBX], uint4 (&bf)[NCBW]) {
+  auto read_b = [&](int st, uint4 (&bf)[NCBW]) {
     const uint8_t* sl = lds + (st % S) * SLOT;
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb)
       bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
-    if constexpr (RB > 0) {
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(sl + AOFF + (row_off + i) * kFrag + 16 * lane);
+  };
+  auto read_a = [&](int st, int i) {
+    if constexpr (kPairA) {
+      const uint8_t* pl = lds + APOFF + ((st >> 1) % Q) * APAIR + (aoff0 ^ ((st & 1) << 6));
+      return *reinterpret_cast<const uint4*>(pl + (row_off + i) * 2 * kFrag);
+    } else {
+      const uint8_t* sl = lds + (st % S) * SLOT;
+      return *reinterpret_cast<const uint4*>(sl + AOFF + (row_off + i) * kFrag + 16 * lane);
     }
   };
-  // One K-stage.  The next stage's fragments are read from LDS before this
-  // stage's MFMAs are issued, so LDS latency hides behind matrix work.  Slot
-  // reuse: stage kt + D refills the slot of stage kt - 1, whose fragments
-  // every wave read (and waited for) before the previous barrier.
-  auto step = [&](int kt, uint4 (&ca)[RBX], uint4 (&cbf)[NCBW], uint4 (&na_)[RBX],
-                  uint4 (&nb_)[NCBW]) {
+  // One K-stage.  The next stage's operands are read from LDS while this
+  // stage's MFMAs run: B into a second register set, A one row block at a
+  // time right after that block's MFMAs (one A register set).  Slot reuse:
+  // stage kt + D refills the B slot of stage kt - 1, whose fragments every
+  // wave read (and waited for) before the previous barrier.
+  uint4 af[RBX];
+  auto step = [&](int kt, uint4 (&cbf)[NCBW], uint4 (&nb_)[NCBW]) {
     if (kt + D < nk) issue(kt + D);
     if (kt + 1 < nk) wait_for(kt + 1);
     wait_lgkm0();      // this wave's reads of stage kt have landed
     stage_barrier();   // stage kt + 1 is visible to every wave
-    if (kt + 1 < nk) read_frags(kt + 1, na_, nb_);
+    const bool more = kt + 1 < nk;
+    if (more) read_b(kt + 1, nb_);
     if constexpr (RB > 0) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
+      for (int i = 0; i < RB; ++i) {
 #pragma unroll
         for (int cb = 0; cb < NCBW; ++cb)
           acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(ca[i]), as_bf16x8(cbf[cb]), acc[i][cb], 0, 0, 0);
+              as_bf16x8(af[i]), as_bf16x8(cbf[cb]), acc[i][cb], 0, 0, 0);
+        if (more) af[i] = read_a(kt + 1, i);
+      }
     }
   };
 
-  uint4 a0[RBX], b0[NCBW], a1[RBX], b1[NCBW];
+  uint4 b0[NCBW], b1[NCBW];
   wait_for(0);
   stage_barrier();
-  read_frags(0, a0, b0);
+  read_b(0, b0);
+  if constexpr (RB > 0) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) af[i] = read_a(0, i);
+  }
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    step(kt, a0, b0, a1, b1);
-    step(kt + 1, a1, b1, a0, b0);
+    step(kt, b0, b1);
+    step(kt + 1, b1, b0);
   }
-  if (kt < nk) step(kt, a0, b0, a1, b1);
+  if (kt < nk) step(kt, b0, b1);
   wait_lgkm0();
   stage_barrier();  // every wave is done with the ring before the next item refills it
 
@@ -276,7 +353,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // bytes.  Rows are padded by 16 bytes so the 4 row groups of a write land
   // on different LDS banks.
   constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per tile row
-  static_assert(16 * NRB * TSTRIDE * 2 <= S * SLOT, "epilogue tile fits the ring");
+  static_assert(16 * NRB * TSTRIDE * 2 <= ring_bytes<MB, S>(), "epilogue tile fits the ring");
   uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
   if constexpr (RB > 0) {
 #pragma unroll
@@ -350,10 +427,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed,
     const uint16_t* __restrict__ lora_t, const uint16_t* __restrict__ lora_b,
     int64_t lora_b_stride, int lora_r) {
-  constexpr int SLOT = (kItemBlocks + MB) * kFrag;
   constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring_bytes<MB, S>()];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntiles = plan[0];
