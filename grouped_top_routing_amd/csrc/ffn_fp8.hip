@@ -136,14 +136,27 @@ __device__ __forceinline__ void fp8_item_rows(const uint16_t* __restrict__ A,
   const int nk = K / kStageK;
   const int na = (NRB - wave + NW - 1) / NW;      // A row blocks this wave loads
 
-  const uint16_t* asrc[AMAX > 0 ? AMAX : 1];
+  // A rows of a 64-k stage go to LDS as whole 128-byte lines: per 16-row
+  // block, rows 0-7 then rows 8-15 (1 KB each), lane l fetching row
+  // 8 hf + l / 8 and the 16-byte chunk that the swizzle places at position
+  // l % 8 of the row (the bf16 GEMM's paired layout, ffn.hip).
+  int asrow[AMAX > 0 ? AMAX : 1][2];
 #pragma unroll
   for (int j = 0; j < AMAX; ++j) {
-    int row = (wave + NW * j) * 16 + r;
-    row = row < nrows ? row : nrows - 1;          // rows past the tile repeat its last row
-    const int src = gather ? gather[row0 + row] / topk : row0 + row;
-    asrc[j] = A + (size_t)src * K + 8 * g;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      int row = (wave + NW * j) * 16 + hf * 8 + (lane >> 3);
+      row = row < nrows ? row : nrows - 1;        // rows past the tile repeat its last row
+      asrow[j][hf] = gather ? gather[row0 + row] / topk : row0 + row;
+    }
   }
+  auto asrc = [&](int j, int hf, int st) {
+    const int rho = hf * 8 + (lane >> 3);
+    return A + (size_t)asrow[j][hf] * K + st * kStageK + 8 * ((lane & 7) ^ ((rho >> 1) & 7));
+  };
+  // this lane's MFMA operand (row r, logical chunk g) inside a row block's
+  // 2 KB; the second 32-k half (chunk 4 + g) flips bit 6
+  const int aoff = (r >> 3) * kFragB + (r & 7) * 128 + ((g ^ ((r >> 1) & 7)) << 4);
   auto weight_row = [&](int cb) {
     if (SWIGLU) {
       const int j = cb % HALF;
@@ -177,8 +190,8 @@ __device__ __forceinline__ void fp8_item_rows(const uint16_t* __restrict__ A,
     for (int j = 0; j < AMAX; ++j)
       if (j < na) {
         const uint32_t ao = a_base + so + NW * j * 2 * kFragB;
-        lds_dma16(asrc[j] + st * kStageK, ao);
-        lds_dma16(asrc[j] + st * kStageK + 32, ao + kFragB);
+        lds_dma16(asrc(j, 0, st), ao);
+        lds_dma16(asrc(j, 1, st), ao + kFragB);
       }
   };
 
@@ -222,7 +235,7 @@ __device__ __forceinline__ void fp8_item_rows(const uint16_t* __restrict__ A,
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
           const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
-              sl + AOFF + (2 * (row_off + i) + h) * kFragB + 16 * lane));
+              sl + AOFF + 2 * (row_off + i) * kFragB + (aoff ^ (h << 6))));
 #pragma unroll
           for (int cb = 0; cb < NCBW; ++cb)
             acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h ? bhi[cb] : blo[cb],
