@@ -79,6 +79,7 @@ __device__ __forceinline__ void stage_barrier() {
 // counts of 63 and more wait for at most 63.
 template <int LO = 0, int HI = 63>
 __device__ __forceinline__ void wait_vm_dyn(int n) {
+  n = __builtin_amdgcn_readfirstlane(n);  // keep the tree on scalar branches
   if constexpr (LO == HI) {
     wait_vm<LO>();
   } else {
@@ -134,6 +135,35 @@ __device__ __forceinline__ void lds_dma16_nt(const void* g, uint32_t lds_addr) {
       : "=&s"(saved)
       : "v"(g), "s"(lds_addr)
       : "memory");
+}
+
+// As lds_dma16 / lds_dma16_nt, addressing base + off with a wave-uniform
+// 64-bit base in SGPRs and a 32-bit per-lane byte offset (one VGPR).
+template <bool NT>
+__device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t off, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t saved;
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(lds_addr), "s"(base)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(lds_addr), "s"(base)
+        : "memory");
+  }
 }
 
 }  // namespace beam

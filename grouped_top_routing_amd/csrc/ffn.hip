@@ -30,11 +30,18 @@
 // * A work item is one (m-tile, n-tile) pair.  A device-built plan cuts each
 //   expert's rows into balanced m-tiles of at most 16*MB rows, so at Beam's
 //   prefill size an expert's rows fit one m-tile and its weights are fetched
-//   once.  Wave w owns NCBW 16-column weight blocks (for gate/up: NCBW/2 gate
-//   blocks and the matching up blocks, so the SwiGLU epilogue is wave-local).
+//   once.  Each wave computes NCBW 16-column weight blocks (for gate/up:
+//   NCBW/2 gate blocks and the matching up blocks, so the SwiGLU epilogue is
+//   wave-local) for its share of the item's rows (see the work split below).
 // * A persistent grid walks the items.  Workgroup b runs on XCD b % 8; items
 //   are dealt so that the n-tiles of one m-tile land on one XCD in the same
-//   round, sharing the gathered A rows through that XCD's L2.
+//   round, sharing the gathered A rows through that XCD's L2.  In the
+//   128/192-row configurations a workgroup issues the first weight stages of
+//   its next item before the current item's epilogue, so its weight stream
+//   keeps running while the outputs are written.
+// * Wave-level values (wave index, wait counts, weight row bases) are kept in
+//   scalar registers: every weight load takes a 64-bit base in SGPRs and one
+//   32-bit lane offset, and the run-time vmcnt waits branch on scalars.
 #include "common.h"
 #include "kernels.h"
 
@@ -91,11 +98,20 @@ struct ItemArgs {
   const uint16_t* lora_t;
   const uint16_t* lora_b;
   int lora_r;
+  // The persistent walk, for configurations that start the workgroup's next
+  // item (q + grid, if below total) while this one finishes: item q is
+  // (m-tile q / nt_n, n-tile q % nt_n), its expert plan_expert[m-tile], and
+  // every item but a workgroup's first (q >= grid) finds its first weight
+  // stages already issued.
+  const uint16_t* W0;      // expert 0's weights
+  int64_t w_expert_stride;
+  const int32_t* plan_expert;
+  int q, grid, total, nt_n;
 };
 
 // Work split inside a workgroup: the kNW waves form RG row groups x CG = kNW /
 // RG column groups.  Every item covers 16 weight-row blocks (kColsGateUp gate
-// + up columns, or kColsDown down columns), so a wave owns NCBW = 16 / CG
+// rows and as many up rows, or kColsDown down rows), so a wave owns NCBW = 16 / CG
 // column blocks and RB of the item's NRB row blocks.  With RG = 2 each A
 // fragment is read from LDS by half the waves and each B fragment by two,
 // which cuts LDS read traffic per MFMA against RG = 1 (every wave reading
@@ -143,6 +159,12 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
   constexpr int WCOLS = CG * HALF * 16;
   constexpr int RBX = RB > 0 ? RB : 1;
+  constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per epilogue tile row
+  // Paired: weight stages of the workgroup's next item issued while this
+  // item's epilogue runs -- as many as fit below the largest epilogue tile.
+  constexpr int kPre = kPairA ? std::min(D, (ring_bytes<MB, S>() - 16 * MB * TSTRIDE * 2) /
+                                                (kItemBlocks * kFrag))
+                              : 0;
   // Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
   // weight stream: weights are then loaded with the non-temporal policy,
   // which measured 6.6 TB/s against 6.1 TB/s with the default one.  The
@@ -182,23 +204,28 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     return a.A + (size_t)asrow[j][hf] * a.K + k0 + 8 * (kPairA ? ((lane & 7) ^ a_swizzle(rho)) : g);
   };
   // the weight row (output column) of lane r in column block cb of group cg
-  auto weight_row = [&](int cb) {
+  // of n-tile ntile
+  auto weight_row_of = [&](int cb, int ntile) {
     if (SWIGLU) {
       const int j = cb % HALF;
-      return a.ntile * WCOLS + cg * HALF * 16 + j * 16 + r + (cb >= HALF ? a.up_row0 : 0);
+      return ntile * WCOLS + cg * HALF * 16 + j * 16 + r + (cb >= HALF ? a.up_row0 : 0);
     }
-    return a.ntile * WCOLS + cg * NCBW * 16 + cb * 16 + r;
+    return ntile * WCOLS + cg * NCBW * 16 + cb * 16 + r;
   };
+  auto weight_row = [&](int cb) { return weight_row_of(cb, a.ntile); };
+  // Weight loads address a wave-uniform base (the lane-0 row of the column
+  // block, in SGPRs) plus one per-lane byte offset shared by every stream:
+  // row-major: row r, k chunk 8g; packed: fragment (wrow/16, stage) holds
+  // this lane's 16 bytes at lane*8, and a row block's fragments follow each
+  // other along k.
+  auto bbase_of = [&](const uint16_t* W, int ntile, int t) {
+    const int wrow0 = weight_row_of(rg + RG * t, ntile) - r;  // uniform
+    return a.packed ? W + (size_t)(wrow0 >> 4) * nk * kFragElems : W + (size_t)wrow0 * a.K;
+  };
+  const uint32_t boff = a.packed ? (uint32_t)lane * 16u : (uint32_t)(r * a.K + 8 * g) * 2u;
   const uint16_t* bsrc[NBL];
 #pragma unroll
-  for (int t = 0; t < NBL; ++t) {
-    const int wrow = weight_row(rg + RG * t);
-    // row-major: row wrow, k chunk 8g; packed: fragment (wrow/16, stage) holds
-    // this lane's 16 bytes at lane*8, and a row block's fragments follow
-    // each other along k.
-    bsrc[t] = a.packed ? a.W + (size_t)((wrow - r) >> 4) * nk * kFragElems + lane * 8
-                       : a.W + (size_t)wrow * a.K + 8 * g;
-  }
+  for (int t = 0; t < NBL; ++t) bsrc[t] = bbase_of(a.W, a.ntile, t);
   const int bstep = a.packed ? kFragElems : kBKS;  // elements per stage along a stream
   // LDS byte offset of the ring (addrspace cast, not the flat address)
   const uint32_t lds0 =
@@ -211,16 +238,17 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // reads logical chunk 4 + g, the same address with bit 6 flipped
   const int aoff0 = (r >> 3) * kFrag + (r & 7) * 128 + ((g ^ a_swizzle(r)) << 4);
 
-  auto issue = [&](int st) {
+  auto issue_b = [&](const uint16_t* const (&src)[NBL], int st) {
     const uint32_t so = (uint32_t)((st % S) * SLOT);
-    const int k0 = st * kBKS;
 #pragma unroll
     for (int t = 0; t < NBL; ++t) {
-      if constexpr (kStreamWeights)
-        lds_dma16_nt(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
-      else
-        lds_dma16(bsrc[t] + (size_t)st * bstep, b_base + so + RG * t * kFrag);
+      lds_dma16_sv<kStreamWeights>(src[t] + (size_t)st * bstep, boff, b_base + so + RG * t * kFrag);
     }
+  };
+  auto issue = [&](int st, bool with_b = true) {
+    const uint32_t so = (uint32_t)((st % S) * SLOT);
+    const int k0 = st * kBKS;
+    if (with_b) issue_b(bsrc, st);
     if constexpr (kPairA) {
       if ((st & 1) == 0) {  // the pair (st, st + 1): 64 k of each A row
         const uint32_t po = (uint32_t)(((st >> 1) % Q) * APAIR);
@@ -245,18 +273,41 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Prologue.  Unpaired: stages 0..D-1 in order.  Paired: the weight loads
+  // of stages 0..D-1 first (but for the first kPre, which every item except
+  // a workgroup's first finds issued by its predecessor), then the A pairs of
+  // those stages.
+  const int dpro = D < nk ? D : nk;
+  if constexpr (kPairA) {
+    if (a.q < a.grid) {  // a workgroup's first item
 #pragma unroll
-  for (int st = 0; st < D; ++st)
-    if (st < nk) issue(st);
+      for (int st = 0; st < kPre; ++st)
+        if (st < nk) issue_b(bsrc, st);
+    }
+#pragma unroll
+    for (int st = kPre; st < D; ++st)
+      if (st < nk) issue_b(bsrc, st);
+#pragma unroll
+    for (int st = 0; st < D; st += 2)
+      if (st < nk) issue(st, false);
+  } else {
+#pragma unroll
+    for (int st = 0; st < D; ++st)
+      if (st < nk) issue(st);
+  }
 
   // wait until stage `st` has landed, given that stages up to
   // min(st + D - 1, nk - 1) have been issued
   auto wait_for = [&](int st) {
     const int ahead = min(D - 1, nk - 1 - st);
     if constexpr (kPairA) {
-      // later stages carry NBL loads each, even ones 2 na more (their pair)
-      const int evens = ((st + ahead) >> 1) - (st >> 1);
-      wait_vm_dyn<0, 15>(ahead * NBL + evens * 2 * na);
+      // Loads younger than stage st's last one: the weight loads of the
+      // loop-issued stages max(st, D - 1) + 1 .. last (the prologue issued
+      // the weights of stages 0..D-1 ahead of every A pair) and the pairs of
+      // the even stages st + 1 .. last.
+      const int last = st + ahead;
+      const int later_b = max(0, last - max(st, D - 1));
+      wait_vm_dyn<0, 15>(later_b * NBL + ((last >> 1) - (st >> 1)) * 2 * na);
     } else {
       if (na == AMAX) wait_stage<D - 1, NBL + AMAX>(ahead);
       else wait_stage<D - 1, NBL + AMAX - 1>(ahead);
@@ -319,6 +370,22 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   wait_lgkm0();
   stage_barrier();  // every wave is done with the ring before the next item refills it
 
+  // Paired: start the next item's weight stream now (B slots 0..kPre-1); the
+  // epilogue below works in the LDS past them.
+  if constexpr (kPairA) {
+    const int qn = a.q + a.grid;
+    if (qn < a.total) {
+      const int tn = qn / a.nt_n;
+      const uint16_t* nw = a.W0 + (size_t)a.plan_expert[tn] * a.w_expert_stride;
+      const uint16_t* nsrc[NBL];
+#pragma unroll
+      for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
+#pragma unroll
+      for (int st = 0; st < kPre; ++st)
+        if (st < nk) issue_b(nsrc, st);
+    }
+  }
+
   // LoRA second factor: rank steps of 32 (ranks past lora_r contribute zeros),
   // operands loaded straight from global memory in the MFMA lane order.
   if constexpr (RB > 0) {
@@ -352,9 +419,9 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // 16-byte row segments, so each output row leaves as 256 or 512 contiguous
   // bytes.  Rows are padded by 16 bytes so the 4 row groups of a write land
   // on different LDS banks.
-  constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per tile row
-  static_assert(16 * NRB * TSTRIDE * 2 <= ring_bytes<MB, S>(), "epilogue tile fits the ring");
-  uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
+  constexpr int TILE0 = kPre * kItemBlocks * kFrag;  // past the next item's weight stages
+  static_assert(TILE0 + 16 * NRB * TSTRIDE * 2 <= ring_bytes<MB, S>(), "epilogue tile fits the ring");
+  uint16_t* tile = reinterpret_cast<uint16_t*>(lds + TILE0);
   if constexpr (RB > 0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -431,7 +498,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[ring_bytes<MB, S>()];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = plan[0];
   const int* plan_expert = plan + 4;
   const int* plan_row0 = plan_expert + max_tiles;
@@ -448,7 +516,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const int e = plan_expert[tile];
     ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0, packed,
                plan_row0[tile], plan_rows[tile], q - tile * nt_n, lora_t,
-               lora_t ? lora_b + (size_t)e * lora_b_stride : nullptr, lora_r};
+               lora_t ? lora_b + (size_t)e * lora_b_stride : nullptr, lora_r, W,
+               w_expert_stride, plan_expert, q, grid, total, nt_n};
     const int nrb = (a.nrows + 15) >> 4;
     gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU>(nrb, a, lds, wave, lane);
   }

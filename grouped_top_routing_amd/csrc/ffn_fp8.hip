@@ -6,8 +6,8 @@
 // w_n,k ~ s_n * q_n,k.  Activations stay bf16: the GEMM streams half the
 // bytes of the bf16 weights, widens the codes to bf16 in registers (exact:
 // every E4M3FN value is a bf16 value) and applies s_n to the fp32 accumulator
-// column in the epilogue, where y_n = s_n * sum_k x_k q_n,k exactly as the
-// dequantised product would be.
+// column in the epilogue: y_n = s_n * sum_k x_k q_n,k, which is the product
+// with the dequantised weights up to fp32 rounding order.
 //
 // Packed layout (moe_quantize_fp8): each expert's [N, K] code matrix is
 // stored as [N/16][K/64][64 lanes][16 bytes]; lane l = r + 16g holds row
@@ -17,8 +17,9 @@
 // of two consecutive 32-wide MFMA k-steps.
 //
 // The pipeline is the bf16 kernel's (direct-to-LDS ring, per-wave vmcnt
-// waits, one barrier per stage, persistent XCD-dealt items, LDS-staged
-// epilogue) with 64-wide k stages and no register look-ahead of fragments.
+// waits, one barrier per stage, persistent XCD-dealt items, row x column wave
+// groups, LDS-staged epilogue) with 64-wide k stages, A rows staged as whole
+// 128-byte lines, and no register look-ahead of fragments.
 #include "common.h"
 #include "kernels.h"
 
