@@ -17,9 +17,10 @@
 //
 // * Weights and activations go global -> LDS with gfx950's direct loads
 //   (global_load_lds_dwordx4: 64 lanes x 16 B into 1 KB of LDS, no VGPRs),
-//   through an S-stage ring.  S-1 stages of 32 k are always in flight; each
-//   wave waits on its own vmcnt and one s_barrier per stage publishes the
-//   stage to the other waves.
+//   through an S-stage ring (stages of 32 k for 64-row tiles, 64 k for
+//   larger ones).  S-1 weight stages are always in flight; each wave waits
+//   on its own vmcnt and one s_barrier per stage publishes the stage to the
+//   other waves.
 // * One 1 KB weight "fragment" is exactly one MFMA operand (16 rows x 32 k,
 //   bf16): lane l fetches row l%16, k chunk (l/16)*8, and later reads the
 //   same 16 bytes back with a conflict-free ds_read_b128 at lane*16.  The
@@ -53,10 +54,10 @@ namespace beam {
 #define BEAM_GEMM_S4 4
 #endif
 #ifndef BEAM_GEMM_S8
-#define BEAM_GEMM_S8 5
+#define BEAM_GEMM_S8 4
 #endif
 #ifndef BEAM_GEMM_S12
-#define BEAM_GEMM_S12 4
+#define BEAM_GEMM_S12 3
 #endif
 #ifndef BEAM_GEMM_MAXMB
 #define BEAM_GEMM_MAXMB 12
@@ -119,24 +120,30 @@ struct ItemArgs {
 constexpr int kItemBlocks = 16;
 
 // LDS ring layouts.  64-row tiles: S slots of [16 B fragments | MB A
-// fragments], every A fragment a 16-row x 32-k MFMA operand (64 bytes of 16
-// rows).  128/192-row tiles stage A 64 k at a time, a "pair" of 32-k stages,
-// so that every A load fetches whole 128-byte lines (the half-line loads cost
-// ~10% at prefill): per 16-row block a pair holds 2 KB, rows 0-7 then rows
-// 8-15, each row's 128 bytes with its 16-byte chunks XOR-swizzled by
-// (row / 2) % 8 so that the MFMA operand reads (16 rows at one logical chunk)
-// hit distinct LDS banks.  B then has its own ring of S 16 KB slots and A a
-// ring of Q pair slots, Q a power of two with 2Q >= S + 1: a pair is refilled
-// only after both of its stages were read and waited for by every wave.
+// fragments] per 32-k stage, every A fragment a 16-row x 32-k MFMA operand
+// (64 bytes of 16 rows).  128/192-row tiles run 64-k stages (two 32-k MFMA
+// sub-steps, one barrier) so that every A load fetches whole 128-byte lines
+// (the half-line loads cost ~10% at prefill): per 16-row block a stage's A
+// holds 2 KB, rows 0-7 then rows 8-15, each row's 128 bytes with its 16-byte
+// chunks XOR-swizzled by (row / 2) % 8 so that the MFMA operand reads (16
+// rows at one logical chunk) hit distinct LDS banks.  Weights then have a
+// ring of S stage slots of 2 x 16 KB, issued S - 1 stages ahead, and A a ring
+// of two slots issued one stage ahead (A comes from L2; the weights from HBM
+// need the deeper look-ahead).
 template <int MB>
 constexpr bool pair_a() { return MB >= 8; }
-template <int S>
-constexpr int pair_slots() { return (S + 2) / 2 <= 2 ? 2 : ((S + 2) / 2 <= 4 ? 4 : 8); }
 __device__ __forceinline__ int a_swizzle(int row) { return (row >> 1) & 7; }
 template <int MB, int S>
 constexpr int ring_bytes() {
-  return pair_a<MB>() ? S * kItemBlocks * kFrag + pair_slots<S>() * MB * 2 * kFrag
+  return pair_a<MB>() ? S * 2 * kItemBlocks * kFrag + 2 * MB * 2 * kFrag
                       : S * (kItemBlocks + MB) * kFrag;
+}
+// LDS of one workgroup: the ring, or the largest epilogue tile (16 * MB rows
+// of the item's columns plus 8 bf16 of padding) if that is larger.
+template <int MB, int S, bool SWIGLU>
+constexpr int lds_bytes() {
+  constexpr int tile = 16 * MB * ((SWIGLU ? kColsGateUp : kColsDown) + 8) * 2;
+  return ring_bytes<MB, S>() > tile ? ring_bytes<MB, S>() : tile;
 }
 
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
@@ -151,19 +158,21 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int D = S - 1;                      // stages in flight ahead of compute
   constexpr bool kPairA = pair_a<MB>();
   constexpr int AOFF = kItemBlocks * kFrag;     // unpaired slot = B fragments, then A fragments
-  constexpr int SLOT = kPairA ? kItemBlocks * kFrag : AOFF + MB * kFrag;  // B stride per stage
-  constexpr int Q = pair_slots<S>();
-  constexpr int APAIR = MB * 2 * kFrag;         // one A pair slot
-  constexpr int APOFF = S * kItemBlocks * kFrag;
-  static_assert(!kPairA || 2 * Q >= S + 1, "a pair slot outlives the stages reading it");
+  constexpr int SLOT = AOFF + MB * kFrag;       // unpaired slot
+  constexpr int BSUB = kItemBlocks * kFrag;     // paired: one 32-k half of a weight stage
+  constexpr int BSTAGE = 2 * BSUB;              // paired: one 64-k weight stage slot
+  constexpr int APAIR = MB * 2 * kFrag;         // paired: one 64-k A slot
+  constexpr int APOFF = S * BSTAGE;             // paired: A ring after the weight ring
+  static_assert(!kPairA || S >= 3, "a weight stage is issued before the A stage waited with it");
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
   constexpr int WCOLS = CG * HALF * 16;
   constexpr int RBX = RB > 0 ? RB : 1;
   constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per epilogue tile row
   // Paired: weight stages of the workgroup's next item issued while this
-  // item's epilogue runs -- as many as fit below the largest epilogue tile.
-  constexpr int kPre = kPairA ? std::min(D, (ring_bytes<MB, S>() - 16 * MB * TSTRIDE * 2) /
-                                                (kItemBlocks * kFrag))
+  // item's epilogue runs -- as many as fit below the largest epilogue tile,
+  // and at most S - 2 (the prologue issues stage S - 1 after the first A).
+  constexpr int kPre = kPairA ? std::min(S - 2, (lds_bytes<MB, S, SWIGLU>() - 16 * MB * TSTRIDE * 2) /
+                                                    BSTAGE)
                               : 0;
   // Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
   // weight stream: weights are then loaded with the non-temporal policy,
@@ -238,109 +247,17 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // reads logical chunk 4 + g, the same address with bit 6 flipped
   const int aoff0 = (r >> 3) * kFrag + (r & 7) * 128 + ((g ^ a_swizzle(r)) << 4);
 
-  auto issue_b = [&](const uint16_t* const (&src)[NBL], int st) {
-    const uint32_t so = (uint32_t)((st % S) * SLOT);
-#pragma unroll
-    for (int t = 0; t < NBL; ++t) {
-      lds_dma16_sv<kStreamWeights>(src[t] + (size_t)st * bstep, boff, b_base + so + RG * t * kFrag);
-    }
-  };
-  auto issue = [&](int st, bool with_b = true) {
-    const uint32_t so = (uint32_t)((st % S) * SLOT);
-    const int k0 = st * kBKS;
-    if (with_b) issue_b(bsrc, st);
-    if constexpr (kPairA) {
-      if ((st & 1) == 0) {  // the pair (st, st + 1): 64 k of each A row
-        const uint32_t po = (uint32_t)(((st >> 1) % Q) * APAIR);
-#pragma unroll
-        for (int j = 0; j < AMAX; ++j)
-          if (j < na) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-              lds_dma16(asrc(j, hf, k0), a_base + po + kNW * j * 2 * kFrag + hf * kFrag);
-          }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < AMAX; ++j)
-        if (j < na) lds_dma16(asrc(j, 0, k0), a_base + so + kNW * j * kFrag);
-    }
-  };
-
   f32x4_t acc[RBX][NCBW];
 #pragma unroll
   for (int i = 0; i < RBX; ++i)
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Prologue.  Unpaired: stages 0..D-1 in order.  Paired: the weight loads
-  // of stages 0..D-1 first (but for the first kPre, which every item except
-  // a workgroup's first finds issued by its predecessor), then the A pairs of
-  // those stages.
-  const int dpro = D < nk ? D : nk;
-  if constexpr (kPairA) {
-    if (a.q < a.grid) {  // a workgroup's first item
-#pragma unroll
-      for (int st = 0; st < kPre; ++st)
-        if (st < nk) issue_b(bsrc, st);
-    }
-#pragma unroll
-    for (int st = kPre; st < D; ++st)
-      if (st < nk) issue_b(bsrc, st);
-#pragma unroll
-    for (int st = 0; st < D; st += 2)
-      if (st < nk) issue(st, false);
-  } else {
-#pragma unroll
-    for (int st = 0; st < D; ++st)
-      if (st < nk) issue(st);
-  }
-
-  // wait until stage `st` has landed, given that stages up to
-  // min(st + D - 1, nk - 1) have been issued
-  auto wait_for = [&](int st) {
-    const int ahead = min(D - 1, nk - 1 - st);
-    if constexpr (kPairA) {
-      // Loads younger than stage st's last one: the weight loads of the
-      // loop-issued stages max(st, D - 1) + 1 .. last (the prologue issued
-      // the weights of stages 0..D-1 ahead of every A pair) and the pairs of
-      // the even stages st + 1 .. last.
-      const int last = st + ahead;
-      const int later_b = max(0, last - max(st, D - 1));
-      wait_vm_dyn<0, 15>(later_b * NBL + ((last >> 1) - (st >> 1)) * 2 * na);
-    } else {
-      if (na == AMAX) wait_stage<D - 1, NBL + AMAX>(ahead);
-      else wait_stage<D - 1, NBL + AMAX - 1>(ahead);
-    }
-  };
-  auto read_b = [&](int st, uint4 (&bf)[NCBW]) {
-    const uint8_t* sl = lds + (st % S) * SLOT;
-#pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb)
-      bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
-  };
-  auto read_a = [&](int st, int i) {
-    if constexpr (kPairA) {
-      const uint8_t* pl = lds + APOFF + ((st >> 1) % Q) * APAIR + (aoff0 ^ ((st & 1) << 6));
-      return *reinterpret_cast<const uint4*>(pl + (row_off + i) * 2 * kFrag);
-    } else {
-      const uint8_t* sl = lds + (st % S) * SLOT;
-      return *reinterpret_cast<const uint4*>(sl + AOFF + (row_off + i) * kFrag + 16 * lane);
-    }
-  };
-  // One K-stage.  The next stage's operands are read from LDS while this
-  // stage's MFMAs run: B into a second register set, A one row block at a
-  // time right after that block's MFMAs (one A register set).  Slot reuse:
-  // stage kt + D refills the B slot of stage kt - 1, whose fragments every
-  // wave read (and waited for) before the previous barrier.
   uint4 af[RBX];
-  auto step = [&](int kt, uint4 (&cbf)[NCBW], uint4 (&nb_)[NCBW]) {
-    if (kt + D < nk) issue(kt + D);
-    if (kt + 1 < nk) wait_for(kt + 1);
-    wait_lgkm0();      // this wave's reads of stage kt have landed
-    stage_barrier();   // stage kt + 1 is visible to every wave
-    const bool more = kt + 1 < nk;
-    if (more) read_b(kt + 1, nb_);
+  uint4 b0[NCBW], b1[NCBW];
+  // MFMAs of one 32-k sub-step on the operands in registers, reading the
+  // next sub-step's A fragments from LDS right after each row block's MFMAs
+  // (one A register set).
+  auto mfmas = [&](const uint4 (&cbf)[NCBW], bool more, auto next_a) {
     if constexpr (RB > 0) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
@@ -348,42 +265,166 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
         for (int cb = 0; cb < NCBW; ++cb)
           acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               as_bf16x8(af[i]), as_bf16x8(cbf[cb]), acc[i][cb], 0, 0, 0);
-        if (more) af[i] = read_a(kt + 1, i);
+        if (more) af[i] = next_a(i);
       }
     }
   };
 
-  uint4 b0[NCBW], b1[NCBW];
-  wait_for(0);
-  stage_barrier();
-  read_b(0, b0);
-  if constexpr (RB > 0) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) af[i] = read_a(0, i);
-  }
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, b0, b1);
-    step(kt + 1, b1, b0);
-  }
-  if (kt < nk) step(kt, b0, b1);
-  wait_lgkm0();
-  stage_barrier();  // every wave is done with the ring before the next item refills it
-
-  // Paired: start the next item's weight stream now (B slots 0..kPre-1); the
-  // epilogue below works in the LDS past them.
   if constexpr (kPairA) {
+    // ---- 128/192-row tiles: 64-k stages ----
+    // Stage P: weights of sub-steps 2P, 2P+1 in slot P % S (issued S - 1
+    // stages ahead), A rows in slot P & 1 (issued one stage ahead).  Order of
+    // issue: prologue B(0..S-2), A(0), A(1), B(S-1); then after the barrier
+    // that publishes stage P + 1: A(P + 2), B(P + S).  So the only loads
+    // younger than A(P + 1) when stage P + 1 is waited for are those of
+    // B(P - 1 + S), and every B(P + 1) is older than A(P + 1).
+    const int nst = nk >> 1;  // K is a multiple of 128: nst >= 2
+    auto issue_b64 = [&](const uint16_t* const (&src)[NBL], int P) {
+      const uint32_t so = (uint32_t)((P % S) * BSTAGE);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < NBL; ++t)
+          lds_dma16_sv<kStreamWeights>(src[t] + (size_t)(2 * P + h) * bstep, boff,
+                                       b_base + so + h * BSUB + RG * t * kFrag);
+    };
+    auto issue_a64 = [&](int P) {
+      const uint32_t po = (uint32_t)((P & 1) * APAIR);
+      const int k0 = P * 2 * kBKS;
+#pragma unroll
+      for (int j = 0; j < AMAX; ++j)
+        if (j < na) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            lds_dma16(asrc(j, hf, k0), a_base + po + kNW * j * 2 * kFrag + hf * kFrag);
+        }
+    };
+    auto read_b64 = [&](int kt, uint4 (&bf)[NCBW]) {
+      const uint8_t* sl = lds + ((kt >> 1) % S) * BSTAGE + (kt & 1) * BSUB;
+#pragma unroll
+      for (int cb = 0; cb < NCBW; ++cb)
+        bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
+    };
+    // sub-step kt's A operand of row block i: logical chunk g of the first
+    // 32 k, 4 + g of the second (the same address with bit 6 flipped)
+    auto read_a64 = [&](int kt, int i) {
+      const uint8_t* pl = lds + APOFF + ((kt >> 1) & 1) * APAIR + (aoff0 ^ ((kt & 1) << 6));
+      return *reinterpret_cast<const uint4*>(pl + (row_off + i) * 2 * kFrag);
+    };
+
+    // Prologue.  Every item except a workgroup's first finds its first kPre
+    // weight stages issued by its predecessor.
+    if (a.q < a.grid) {
+#pragma unroll
+      for (int P = 0; P < kPre; ++P) issue_b64(bsrc, P);
+    }
+#pragma unroll
+    for (int P = kPre; P < S - 1; ++P)
+      if (P < nst) issue_b64(bsrc, P);
+    issue_a64(0);
+    issue_a64(1);
+    if (S - 1 < nst) issue_b64(bsrc, S - 1);
+    wait_vm_dyn<0, 15>(2 * na + (S - 1 < nst ? 2 * NBL : 0));  // stage 0 landed
+    stage_barrier();
+    read_b64(0, b0);
+    if constexpr (RB > 0) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) af[i] = read_a64(0, i);
+    }
+    for (int P = 0; P < nst; ++P) {
+      const int kt = 2 * P;
+      // sub-step 2P: the operands of 2P + 1 are in the same, published stage
+      read_b64(kt + 1, b1);
+      mfmas(b0, true, [&](int i) { return read_a64(kt + 1, i); });
+      // sub-step 2P + 1: publish stage P + 1, refill stage P's slots
+      const bool more = P + 1 < nst;
+      if (more) {
+        if (P - 1 + S < nst) wait_vm<2 * NBL>();  // stage P + 1 landed
+        else wait_vm<0>();
+        wait_lgkm0();     // this wave's reads of stage P have landed
+        stage_barrier();  // stage P + 1 is visible; stage P's slots are free
+        if (P + 2 < nst) issue_a64(P + 2);
+        if (P + S < nst) issue_b64(bsrc, P + S);
+        read_b64(kt + 2, b0);
+      }
+      mfmas(b1, more, [&](int i) { return read_a64(kt + 2, i); });
+    }
+    wait_lgkm0();
+    stage_barrier();  // every wave is done with the ring
+
+    // Start the next item's weight stream now (stage slots 0..kPre-1); the
+    // epilogue below works in the LDS past them.
     const int qn = a.q + a.grid;
-    if (qn < a.total) {
+    if (kPre > 0 && qn < a.total) {
       const int tn = qn / a.nt_n;
       const uint16_t* nw = a.W0 + (size_t)a.plan_expert[tn] * a.w_expert_stride;
       const uint16_t* nsrc[NBL];
 #pragma unroll
       for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
 #pragma unroll
-      for (int st = 0; st < kPre; ++st)
-        if (st < nk) issue_b(nsrc, st);
+      for (int P = 0; P < kPre; ++P) issue_b64(nsrc, P);
     }
+  } else {
+    // ---- 64-row tiles: 32-k stages, B and A of a stage in one slot ----
+    auto issue = [&](int st) {
+      const uint32_t so = (uint32_t)((st % S) * SLOT);
+#pragma unroll
+      for (int t = 0; t < NBL; ++t)
+        lds_dma16_sv<kStreamWeights>(bsrc[t] + (size_t)st * bstep, boff,
+                                     b_base + so + RG * t * kFrag);
+#pragma unroll
+      for (int j = 0; j < AMAX; ++j)
+        if (j < na) lds_dma16(asrc(j, 0, st * kBKS), a_base + so + kNW * j * kFrag);
+    };
+    // wait until stage `st` has landed, given that stages up to
+    // min(st + D - 1, nk - 1) have been issued
+    auto wait_for = [&](int st) {
+      const int ahead = min(D - 1, nk - 1 - st);
+      if (na == AMAX) wait_stage<D - 1, NBL + AMAX>(ahead);
+      else wait_stage<D - 1, NBL + AMAX - 1>(ahead);
+    };
+    auto read_b = [&](int st, uint4 (&bf)[NCBW]) {
+      const uint8_t* sl = lds + (st % S) * SLOT;
+#pragma unroll
+      for (int cb = 0; cb < NCBW; ++cb)
+        bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
+    };
+    auto read_a = [&](int st, int i) {
+      const uint8_t* sl = lds + (st % S) * SLOT;
+      return *reinterpret_cast<const uint4*>(sl + AOFF + (row_off + i) * kFrag + 16 * lane);
+    };
+    // One K-stage.  The next stage's operands are read from LDS while this
+    // stage's MFMAs run.  Slot reuse: stage kt + D refills the slot of stage
+    // kt - 1, whose fragments every wave read (and waited for) before the
+    // previous barrier.
+    auto step = [&](int kt, const uint4 (&cbf)[NCBW], uint4 (&nb_)[NCBW]) {
+      if (kt + D < nk) issue(kt + D);
+      if (kt + 1 < nk) wait_for(kt + 1);
+      wait_lgkm0();      // this wave's reads of stage kt have landed
+      stage_barrier();   // stage kt + 1 is visible to every wave
+      const bool more = kt + 1 < nk;
+      if (more) read_b(kt + 1, nb_);
+      mfmas(cbf, more, [&](int i) { return read_a(kt + 1, i); });
+    };
+
+#pragma unroll
+    for (int st = 0; st < D; ++st)
+      if (st < nk) issue(st);
+    wait_for(0);
+    stage_barrier();
+    read_b(0, b0);
+    if constexpr (RB > 0) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) af[i] = read_a(0, i);
+    }
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, b0, b1);
+      step(kt + 1, b1, b0);
+    }
+    if (kt < nk) step(kt, b0, b1);
+    wait_lgkm0();
+    stage_barrier();  // every wave is done with the ring before the next item refills it
   }
 
   // LoRA second factor: rank steps of 32 (ranks past lora_r contribute zeros),
@@ -419,8 +460,8 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // 16-byte row segments, so each output row leaves as 256 or 512 contiguous
   // bytes.  Rows are padded by 16 bytes so the 4 row groups of a write land
   // on different LDS banks.
-  constexpr int TILE0 = kPre * kItemBlocks * kFrag;  // past the next item's weight stages
-  static_assert(TILE0 + 16 * NRB * TSTRIDE * 2 <= ring_bytes<MB, S>(), "epilogue tile fits the ring");
+  constexpr int TILE0 = kPre * BSTAGE;  // past the next item's weight stages
+  static_assert(TILE0 + 16 * NRB * TSTRIDE * 2 <= lds_bytes<MB, S, SWIGLU>(), "epilogue tile fits");
   uint16_t* tile = reinterpret_cast<uint16_t*>(lds + TILE0);
   if constexpr (RB > 0) {
 #pragma unroll
@@ -496,7 +537,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     int64_t lora_b_stride, int lora_r) {
   constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring_bytes<MB, S>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<MB, S, SWIGLU>()];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
