@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--workload", default="prefill", choices=["decode", "mid", "prefill", "skew"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the T=512 and skewed T=16384 measurements")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight variant")
     p.add_argument("--no-lora", action="store_true", help="skip the expert-LoRA variant")
@@ -102,7 +104,7 @@ def algorithmic(w, counts, fmt="bf16"):
             "expert_flops": flops, "gate_up_flops": K * T * 2 * 2 * H * I}
 
 
-def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16"):
+def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", rowmajor=True):
     """Times `steps` staged layer passes; returns timing dict and routing.
     fmt "bf16": fragment-packed bf16 expert weights; "fp8": E4M3FN codes
     with per-row scales."""
@@ -178,7 +180,7 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16"):
         layer_ms, rowmajor_ms = (time.perf_counter() - t1) * 1e3 / steps, None
     else:
         layer_ms = time_layer(wgu, wd, lay)
-        rowmajor_ms = (None if args.no_row_major_ref else
+        rowmajor_ms = (None if args.no_row_major_ref or not rowmajor else
                        time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
             "device_step_ms": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
@@ -344,6 +346,28 @@ def main():
                             "touched_experts": da["touched"],
                             "stage_ms": {k: round(v, 4) for k, v in d["stage_ms"].items()}}
         del d
+    if not args.no_other_workloads:
+        # the other shapes of the layer's operating range: a 512-token batch
+        # (HBM-bound) and a skewed 16K-token batch (MFMA-bound; inputs shifted
+        # so that 16 hot experts gain +2.0 on their router logits)
+        result["other_workloads"] = {}
+        for name in [n for n in ("mid", "skew") if n != args.workload]:
+            print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+            o = run_workload(name, wts, args, max(args.steps // 2, 5), 3, gtr, synth, torch,
+                             rowmajor=False)
+            oa = algorithmic(o["w"], o["counts"])
+            t_s = o["ms_per_step"] * 1e-3
+            result["other_workloads"][name] = {
+                "tokens": o["w"].T, "ms_per_step": round(o["ms_per_step"], 4),
+                "tokens_per_s": round(o["w"].T / t_s, 1),
+                "hbm_frac": round(oa["layer_bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4),
+                "bf16_mfma_frac": round(oa["expert_flops"] / t_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "roofline_frac": round(max(oa["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                           oa["expert_flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t_s, 4),
+                "touched_experts": oa["touched"],
+                "max_rows_per_expert": int(o["counts"].max()),
+                "stage_ms": {k: round(v, 4) for k, v in o["stage_ms"].items()}}
+            del o
     if not args.no_fp8:
         # the FP8 per-channel variant of the same layer (weights quantised once
         # at load time); reported beside the bf16 headline, never in `value`
