@@ -140,12 +140,15 @@ def test_expert_ffn(tiny):
 
 
 @pytest.mark.parametrize("hot_rows,T", [(1, 64), (17, 64), (40, 200), (130, 700), (300, 1024),
-                                        (1000, 2048), (700, 3072), (2500, 4096)])
+                                        (1000, 2048), (700, 3072), (2500, 4096),
+                                        (3000, 16384)])
 def test_expert_ffn_ragged_tiles(tiny, hot_rows, T):
     # one expert gets `hot_rows` rows, the rest spread thinly: m-tiles with
     # ragged tails, experts with a single row, and every m-tile height the
     # library picks from the mean rows per expert (up to 1024 tokens -> 64-row
-    # tiles, 2048 -> 128, 3072 and 4096 -> 192)
+    # tiles, 2048 -> 128, 3072 and up -> 192; at 16384 tokens there are ~3
+    # times more m-tiles than workgroups, so each workgroup runs several items
+    # back to back and starts each next item's weight stream early)
     say(f"[expert_ffn] ragged hot_rows={hot_rows} T={T}")
     npd = tiny["np"]
     rng = np.random.default_rng(hot_rows)
@@ -266,7 +269,7 @@ def test_pack_weights_is_the_documented_permutation(tiny):
         assert np.array_equal(np.sort(w.ravel()), np.sort(P.view(torch.int16).cpu().numpy().ravel()))
 
 
-@pytest.mark.parametrize("T", [64, 128, 700, 2048])
+@pytest.mark.parametrize("T", [64, 128, 700, 2048, 16384])
 def test_packed_layout_matches_row_major_bitwise(tiny, T):
     # same operands, same k order: the packed path must reproduce the row-major
     # path bit for bit at every m-tile height
