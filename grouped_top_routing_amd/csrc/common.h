@@ -100,6 +100,14 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   }
 }
 
+// Two E4M3FN codes (bytes 0-1 of w, or bytes 2-3 for HI) widened to two bf16
+// values in one 32-bit word, the lower code in the low half.  Exact: every
+// E4M3FN value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // One direct global -> LDS load: lane l's 16 bytes at `g` land at LDS byte
 // address lds_addr + 16*l (lds_addr must be wave-uniform; it goes in M0).
 // Issued from inline asm so the compiler's own wait-count pass does not see

@@ -108,6 +108,9 @@ struct ItemArgs {
   int64_t w_expert_stride;
   const int32_t* plan_expert;
   int q, grid, total, nt_n;
+  // fp8 weights: this expert's fp32 scale per weight row (W then holds the
+  // E4M3FN codes in the fp8 fragment layout); null for bf16 weights
+  const float* scale;
 };
 
 // Work split inside a workgroup: the kNW waves form RG row groups x CG = kNW /
@@ -133,23 +136,23 @@ constexpr int kItemBlocks = 16;
 template <int MB>
 constexpr bool pair_a() { return MB >= 8; }
 __device__ __forceinline__ int a_swizzle(int row) { return (row >> 1) & 7; }
-template <int MB, int S>
+template <int MB, int S, bool F8 = false>
 constexpr int ring_bytes() {
-  return pair_a<MB>() ? S * 2 * kItemBlocks * kFrag + 2 * MB * 2 * kFrag
+  return pair_a<MB>() ? S * (F8 ? 1 : 2) * kItemBlocks * kFrag + 2 * MB * 2 * kFrag
                       : S * (kItemBlocks + MB) * kFrag;
 }
 // LDS of one workgroup: the ring, or the largest epilogue tile (16 * MB rows
 // of the item's columns plus 8 bf16 of padding) if that is larger.
-template <int MB, int S, bool SWIGLU>
+template <int MB, int S, bool SWIGLU, bool F8 = false>
 constexpr int lds_bytes() {
   constexpr int tile = 16 * MB * ((SWIGLU ? kColsGateUp : kColsDown) + 8) * 2;
-  return ring_bytes<MB, S>() > tile ? ring_bytes<MB, S>() : tile;
+  return ring_bytes<MB, S, F8>() > tile ? ring_bytes<MB, S, F8>() : tile;
 }
 
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
 // this wave computes RB blocks starting at block row_off.  MB sizes the LDS
 // ring; fragments of blocks NRB..MB-1 are not loaded.
-template <int NRB, int RB, int MB, int kNW, int RG, int S, bool SWIGLU>
+template <int NRB, int RB, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
 __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, int wave, int lane,
                                                int row_off) {
   constexpr int CG = kNW / RG;
@@ -160,7 +163,8 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int AOFF = kItemBlocks * kFrag;     // unpaired slot = B fragments, then A fragments
   constexpr int SLOT = AOFF + MB * kFrag;       // unpaired slot
   constexpr int BSUB = kItemBlocks * kFrag;     // paired: one 32-k half of a weight stage
-  constexpr int BSTAGE = 2 * BSUB;              // paired: one 64-k weight stage slot
+  constexpr int BSTAGE = F8 ? BSUB : 2 * BSUB;  // paired: one 64-k weight stage slot
+  static_assert(!F8 || kPairA, "fp8 weights run the 64-k stage pipeline only");
   constexpr int APAIR = MB * 2 * kFrag;         // paired: one 64-k A slot
   constexpr int APOFF = S * BSTAGE;             // paired: A ring after the weight ring
   static_assert(!kPairA || S >= 3, "a weight stage is issued before the A stage waited with it");
@@ -171,7 +175,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // Paired: weight stages of the workgroup's next item issued while this
   // item's epilogue runs -- as many as fit below the largest epilogue tile,
   // and at most S - 2 (the prologue issues stage S - 1 after the first A).
-  constexpr int kPre = kPairA ? std::min(S - 2, (lds_bytes<MB, S, SWIGLU>() - 16 * MB * TSTRIDE * 2) /
+  constexpr int kPre = kPairA ? std::min(S - 2, (lds_bytes<MB, S, SWIGLU, F8>() - 16 * MB * TSTRIDE * 2) /
                                                     BSTAGE)
                               : 0;
   // Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
@@ -225,17 +229,26 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // Weight loads address a wave-uniform base (the lane-0 row of the column
   // block, in SGPRs) plus one per-lane byte offset shared by every stream:
   // row-major: row r, k chunk 8g; packed: fragment (wrow/16, stage) holds
-  // this lane's 16 bytes at lane*8, and a row block's fragments follow each
-  // other along k.
-  auto bbase_of = [&](const uint16_t* W, int ntile, int t) {
+  // this lane's 16 bytes at lane*16, and a row block's fragments follow each
+  // other along k (bf16: one per 32 k; fp8: one per 64 k).
+  auto bbase_of = [&](const uint16_t* W, int ntile, int t) -> const uint8_t* {
     const int wrow0 = weight_row_of(rg + RG * t, ntile) - r;  // uniform
-    return a.packed ? W + (size_t)(wrow0 >> 4) * nk * kFragElems : W + (size_t)wrow0 * a.K;
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
+    if constexpr (F8) return w + (size_t)(wrow0 >> 4) * (nk >> 1) * kFrag;
+    return a.packed ? w + (size_t)(wrow0 >> 4) * nk * kFrag : w + (size_t)wrow0 * a.K * 2;
   };
   const uint32_t boff = a.packed ? (uint32_t)lane * 16u : (uint32_t)(r * a.K + 8 * g) * 2u;
-  const uint16_t* bsrc[NBL];
+  const uint8_t* bsrc[NBL];
 #pragma unroll
   for (int t = 0; t < NBL; ++t) bsrc[t] = bbase_of(a.W, a.ntile, t);
-  const int bstep = a.packed ? kFragElems : kBKS;  // elements per stage along a stream
+  const int bstep = a.packed ? kFrag : kBKS * 2;  // bf16: bytes per 32-k stage along a stream
+  // fp8: the fp32 scale of each of this lane's weight-row columns, applied
+  // to the accumulators after the k loop
+  float wscale[F8 ? NCBW : 1];
+  if constexpr (F8) {
+#pragma unroll
+    for (int cb = 0; cb < NCBW; ++cb) wscale[cb] = a.scale[weight_row(cb)];
+  }
   // LDS byte offset of the ring (addrspace cast, not the flat address)
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
@@ -279,14 +292,24 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     // younger than A(P + 1) when stage P + 1 is waited for are those of
     // B(P - 1 + S), and every B(P + 1) is older than A(P + 1).
     const int nst = nk >> 1;  // K is a multiple of 128: nst >= 2
-    auto issue_b64 = [&](const uint16_t* const (&src)[NBL], int P) {
+    // weight loads of one stage per wave: bf16 two 1 KB fragments (32 k
+    // each) per column block it loads, fp8 one (64 k)
+    constexpr int kStageLoads = F8 ? NBL : 2 * NBL;
+    auto issue_b64 = [&](const uint8_t* const (&src)[NBL], int P) {
       const uint32_t so = (uint32_t)((P % S) * BSTAGE);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
+      if constexpr (F8) {
 #pragma unroll
         for (int t = 0; t < NBL; ++t)
-          lds_dma16_sv<kStreamWeights>(src[t] + (size_t)(2 * P + h) * bstep, boff,
-                                       b_base + so + h * BSUB + RG * t * kFrag);
+          lds_dma16_sv<kStreamWeights>(src[t] + (size_t)P * kFrag, boff,
+                                       b_base + so + RG * t * kFrag);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < NBL; ++t)
+            lds_dma16_sv<kStreamWeights>(src[t] + (size_t)(2 * P + h) * bstep, boff,
+                                         b_base + so + h * BSUB + RG * t * kFrag);
+      }
     };
     auto issue_a64 = [&](int P) {
       const uint32_t po = (uint32_t)((P & 1) * APAIR);
@@ -300,10 +323,22 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
         }
     };
     auto read_b64 = [&](int kt, uint4 (&bf)[NCBW]) {
-      const uint8_t* sl = lds + ((kt >> 1) % S) * BSTAGE + (kt & 1) * BSUB;
+      if constexpr (F8) {
+        // the fragment's first 512 bytes hold every lane's 8 codes of the
+        // first 32 k, the next 512 those of the second; widened to bf16
+        const uint8_t* sl = lds + ((kt >> 1) % S) * BSTAGE + (kt & 1) * 512;
 #pragma unroll
-      for (int cb = 0; cb < NCBW; ++cb)
-        bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
+        for (int cb = 0; cb < NCBW; ++cb) {
+          const uint2 c = *reinterpret_cast<const uint2*>(sl + (cg * NCBW + cb) * kFrag + 8 * lane);
+          bf[cb] = make_uint4(fp8x2_to_bf16x2<false>(c.x), fp8x2_to_bf16x2<true>(c.x),
+                              fp8x2_to_bf16x2<false>(c.y), fp8x2_to_bf16x2<true>(c.y));
+        }
+      } else {
+        const uint8_t* sl = lds + ((kt >> 1) % S) * BSTAGE + (kt & 1) * BSUB;
+#pragma unroll
+        for (int cb = 0; cb < NCBW; ++cb)
+          bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
+      }
     };
     // sub-step kt's A operand of row block i: logical chunk g of the first
     // 32 k, 4 + g of the second (the same address with bit 6 flipped)
@@ -324,7 +359,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     issue_a64(0);
     issue_a64(1);
     if (S - 1 < nst) issue_b64(bsrc, S - 1);
-    wait_vm_dyn<0, 15>(2 * na + (S - 1 < nst ? 2 * NBL : 0));  // stage 0 landed
+    wait_vm_dyn<0, 15>(2 * na + (S - 1 < nst ? kStageLoads : 0));  // stage 0 landed
     stage_barrier();
     read_b64(0, b0);
     if constexpr (RB > 0) {
@@ -339,7 +374,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       // sub-step 2P + 1: publish stage P + 1, refill stage P's slots
       const bool more = P + 1 < nst;
       if (more) {
-        if (P - 1 + S < nst) wait_vm<2 * NBL>();  // stage P + 1 landed
+        if (P - 1 + S < nst) wait_vm<kStageLoads>();  // stage P + 1 landed
         else wait_vm<0>();
         wait_lgkm0();     // this wave's reads of stage P have landed
         stage_barrier();  // stage P + 1 is visible; stage P's slots are free
@@ -351,6 +386,12 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     }
     wait_lgkm0();
     stage_barrier();  // every wave is done with the ring
+    if constexpr (F8 && RB > 0) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] *= wscale[cb];
+    }
 
     // Start the next item's weight stream now (stage slots 0..kPre-1); the
     // epilogue below works in the LDS past them.
@@ -358,7 +399,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     if (kPre > 0 && qn < a.total) {
       const int tn = qn / a.nt_n;
       const uint16_t* nw = a.W0 + (size_t)a.plan_expert[tn] * a.w_expert_stride;
-      const uint16_t* nsrc[NBL];
+      const uint8_t* nsrc[NBL];
 #pragma unroll
       for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
 #pragma unroll
@@ -429,7 +470,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 
   // LoRA second factor: rank steps of 32 (ranks past lora_r contribute zeros),
   // operands loaded straight from global memory in the MFMA lane order.
-  if constexpr (RB > 0) {
+  if constexpr (RB > 0 && !F8) {
     if (a.lora_t) {
       const int R = a.lora_r;
       for (int k0 = 0; k0 < R; k0 += 32) {
@@ -461,7 +502,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // bytes.  Rows are padded by 16 bytes so the 4 row groups of a write land
   // on different LDS banks.
   constexpr int TILE0 = kPre * BSTAGE;  // past the next item's weight stages
-  static_assert(TILE0 + 16 * NRB * TSTRIDE * 2 <= lds_bytes<MB, S, SWIGLU>(), "epilogue tile fits");
+  static_assert(TILE0 + 16 * NRB * TSTRIDE * 2 <= lds_bytes<MB, S, SWIGLU, F8>(), "epilogue tile fits");
   uint16_t* tile = reinterpret_cast<uint16_t*>(lds + TILE0);
   if constexpr (RB > 0) {
 #pragma unroll
@@ -503,41 +544,41 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 
 // Item with NRB live row blocks: row group 0 takes the first ceil(NRB / RG)
 // blocks, row group 1 the rest.
-template <int NRB, int MB, int kNW, int RG, int S, bool SWIGLU>
+template <int NRB, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
 __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int wave, int lane) {
   if constexpr (RG == 1) {
-    gemm_item_rows<NRB, NRB, MB, kNW, 1, S, SWIGLU>(a, lds, wave, lane, 0);
+    gemm_item_rows<NRB, NRB, MB, kNW, 1, S, SWIGLU, F8>(a, lds, wave, lane, 0);
   } else {
     static_assert(RG == 2, "one or two row groups");
     constexpr int RB0 = (NRB + 1) / 2;
     if (wave < kNW / 2)
-      gemm_item_rows<NRB, RB0, MB, kNW, 2, S, SWIGLU>(a, lds, wave, lane, 0);
+      gemm_item_rows<NRB, RB0, MB, kNW, 2, S, SWIGLU, F8>(a, lds, wave, lane, 0);
     else
-      gemm_item_rows<NRB, NRB - RB0, MB, kNW, 2, S, SWIGLU>(a, lds, wave, lane, RB0);
+      gemm_item_rows<NRB, NRB - RB0, MB, kNW, 2, S, SWIGLU, F8>(a, lds, wave, lane, RB0);
   }
 }
 
-template <int N, int MB, int kNW, int RG, int S, bool SWIGLU>
+template <int N, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
 __device__ __forceinline__ void gemm_item_dispatch(int nrb, const ItemArgs& a, uint8_t* lds,
                                                    int wave, int lane) {
   if constexpr (N > MB) {
     return;
   } else {
-    if (nrb == N) gemm_item<N, MB, kNW, RG, S, SWIGLU>(a, lds, wave, lane);
-    else gemm_item_dispatch<N + 1, MB, kNW, RG, S, SWIGLU>(nrb, a, lds, wave, lane);
+    if (nrb == N) gemm_item<N, MB, kNW, RG, S, SWIGLU, F8>(a, lds, wave, lane);
+    else gemm_item_dispatch<N + 1, MB, kNW, RG, S, SWIGLU, F8>(nrb, a, lds, wave, lane);
   }
 }
 
-template <int MB, int kNW, int RG, int S, bool SWIGLU>
+template <int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
 __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
     const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed,
     const uint16_t* __restrict__ lora_t, const uint16_t* __restrict__ lora_b,
-    int64_t lora_b_stride, int lora_r) {
+    int64_t lora_b_stride, int lora_r, const float* __restrict__ scales, int64_t scale_stride) {
   constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<MB, S, SWIGLU>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<MB, S, SWIGLU, F8>()];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -558,9 +599,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0, packed,
                plan_row0[tile], plan_rows[tile], q - tile * nt_n, lora_t,
                lora_t ? lora_b + (size_t)e * lora_b_stride : nullptr, lora_r, W,
-               w_expert_stride, plan_expert, q, grid, total, nt_n};
+               w_expert_stride, plan_expert, q, grid, total, nt_n,
+               F8 ? scales + (size_t)e * scale_stride : nullptr};
     const int nrb = (a.nrows + 15) >> 4;
-    gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU>(nrb, a, lds, wave, lane);
+    gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU, F8>(nrb, a, lds, wave, lane);
   }
 }
 
@@ -629,13 +671,14 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
 // S * (16 + MB) KB.  Small m-tiles use 4 waves and fit two workgroups per CU;
 // large ones use 8 waves (two per SIMD) in one workgroup, as 2 row groups x 4
 // column groups.
-template <int MB, int NW, int RG, int S, bool SWIGLU>
+template <int MB, int NW, int RG, int S, bool SWIGLU, bool F8 = false>
 static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int topk,
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                 int packed, const LoraArgs& lora, int64_t max_items,
-                                hipStream_t stream) {
-  auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU>;
+                                hipStream_t stream, const float* scales = nullptr,
+                                int64_t scale_stride = 0) {
+  auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU, F8>;
   static int per_cu = 0;  // resident workgroups per CU, fixed per build
   static int cus = 0;
   if (per_cu == 0) {
@@ -654,7 +697,7 @@ static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int to
   if (grid < 8) grid = 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, stream, A, gather, topk, W,
                      wstride, C, plan, max_tiles, K, n_out, up_row0, packed, lora.t, lora.b,
-                     lora.b_stride, lora.rank);
+                     lora.b_stride, lora.rank, scales, scale_stride);
   return hipGetLastError();
 }
 
@@ -711,6 +754,43 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
       return hipErrorInvalidValue;
   }
 #undef BEAM_STREAM_CASE
+}
+
+// FP8 (E4M3FN) weights through the same 64-k stage pipeline: a weight stage
+// is one 1 KB fragment of 16 rows x 64 k per row block (16 KB per stage),
+// widened to bf16 in registers, and the per-row scales multiply the fp32
+// accumulators after the k loop.  128- and 192-row tiles.
+#ifndef BEAM_FP8P_S8
+#define BEAM_FP8P_S8 5
+#endif
+#ifndef BEAM_FP8P_S12
+#define BEAM_FP8P_S12 5
+#endif
+hipError_t launch_grouped_gemm_fp8_paired(int mb, bool swiglu, const uint16_t* A,
+                                          const int32_t* gather, int topk, const uint8_t* Q,
+                                          const float* scales, int64_t qstride, int N, uint16_t* C,
+                                          const int32_t* plan, int max_tiles, int K, int n_out,
+                                          int up_row0, int64_t max_items, hipStream_t stream) {
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(Q);
+  const int64_t wstride = qstride / 2;  // in 2-byte units: N * K codes per expert
+  const LoraArgs none{};
+#define BEAM_FP8P_CASE(MBV, SV)                                                                \
+  case MBV:                                                                                     \
+    return swiglu ? launch_stream<MBV, 8, 2, SV, true, true>(A, gather, topk, W, wstride, C,    \
+                                                             plan, max_tiles, K, n_out,         \
+                                                             up_row0, 1, none, max_items,       \
+                                                             stream, scales, N)                 \
+                  : launch_stream<MBV, 8, 2, SV, false, true>(A, gather, topk, W, wstride, C,   \
+                                                              plan, max_tiles, K, n_out,        \
+                                                              up_row0, 1, none, max_items,      \
+                                                              stream, scales, N);
+  switch (mb) {
+    BEAM_FP8P_CASE(8, BEAM_FP8P_S8)
+    BEAM_FP8P_CASE(12, BEAM_FP8P_S12)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef BEAM_FP8P_CASE
 }
 
 }  // namespace beam

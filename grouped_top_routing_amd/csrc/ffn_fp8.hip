@@ -10,16 +10,19 @@
 // with the dequantised weights up to fp32 rounding order.
 //
 // Packed layout (moe_quantize_fp8): each expert's [N, K] code matrix is
-// stored as [N/16][K/64][64 lanes][16 bytes]; lane l = r + 16g holds row
-// 16b + r, bytes 0..7 at k = 64s + 8g .. +7 and bytes 8..15 at
-// k = 64s + 32 + 8g .. +7.  One 1 KB direct load therefore brings 16 rows x
-// 64 k, and its two 8-byte halves line up with the bf16 activation operands
-// of two consecutive 32-wide MFMA k-steps.
+// stored as [N/16][K/64][2][64 lanes][8 bytes]; entry (b, s, h, l) holds row
+// 16b + l%16 at k = 64s + 32h + 8(l/16) .. +7.  One 1 KB direct load
+// therefore brings 16 rows x 64 k, and its two 512-byte halves are the
+// operands of two consecutive 32-wide MFMA k-steps in the
+// v_mfma_f32_16x16x32_bf16 lane order, each read with a linear 8-byte LDS
+// read per lane.
 //
-// The pipeline is the bf16 kernel's (direct-to-LDS ring, per-wave vmcnt
-// waits, one barrier per stage, persistent XCD-dealt items, row x column wave
-// groups, LDS-staged epilogue) with 64-wide k stages, A rows staged as whole
-// 128-byte lines, and no register look-ahead of fragments.
+// Batches of 128/192-row m-tiles run the bf16 kernel's 64-k stage pipeline
+// (ffn.hip, launch_grouped_gemm_fp8_paired).  This file holds the quantiser
+// and the 32-row configuration for decode-sized batches: a direct-to-LDS
+// ring of 64-k stages with per-wave vmcnt waits, one barrier per stage,
+// persistent XCD-dealt items and an LDS-staged epilogue, two workgroups per
+// CU.
 #include "common.h"
 #include "kernels.h"
 
@@ -102,7 +105,9 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
       }
       out[i] = word;
     }
-    st16(Q + (size_t)c * 16, make_uint4(out[0], out[1], out[2], out[3]));
+    uint8_t* frag = Q + (size_t)st * kFragB + l * 8;
+    *reinterpret_cast<uint2*>(frag) = make_uint2(out[0], out[1]);        // k 64st + 8g ..
+    *reinterpret_cast<uint2*>(frag + 512) = make_uint2(out[2], out[3]);  // k 64st + 32 + 8g ..
   }
 }
 
@@ -217,9 +222,10 @@ __device__ __forceinline__ void fp8_item_rows(const uint16_t* __restrict__ A,
       bf16x8_t blo[NCBW], bhi[NCBW];
 #pragma unroll
       for (int cb = 0; cb < NCBW; ++cb) {
-        const uint4 raw =
-            *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFragB + 16 * lane);
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint2 lo = *reinterpret_cast<const uint2*>(sl + (cg * NCBW + cb) * kFragB + 8 * lane);
+        const uint2 hi =
+            *reinterpret_cast<const uint2*>(sl + (cg * NCBW + cb) * kFragB + 512 + 8 * lane);
+        const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -295,21 +301,9 @@ __device__ __forceinline__ void fp8_item(const uint16_t* A, const int32_t* gathe
                                          const uint8_t* Qe, const float* Se, uint16_t* C, int K,
                                          int n_out, int up_row0, int row0, int nrows, int ntile,
                                          uint8_t* lds, int wave, int lane) {
-  if constexpr (RG == 1) {
-    fp8_item_rows<NRB, NRB, MB, NW, 1, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out, up_row0,
-                                                  row0, nrows, ntile, lds, wave, lane, 0);
-  } else {
-    static_assert(RG == 2, "one or two row groups");
-    constexpr int RB0 = (NRB + 1) / 2;
-    if (wave < NW / 2)
-      fp8_item_rows<NRB, RB0, MB, NW, 2, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out,
-                                                    up_row0, row0, nrows, ntile, lds, wave, lane,
-                                                    0);
-    else
-      fp8_item_rows<NRB, NRB - RB0, MB, NW, 2, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out,
-                                                          up_row0, row0, nrows, ntile, lds, wave,
-                                                          lane, RB0);
-  }
+  static_assert(RG == 1, "the 32-row configuration has one row group");
+  fp8_item_rows<NRB, NRB, MB, NW, 1, S, SWIGLU>(A, gather, topk, Qe, Se, C, K, n_out, up_row0, row0,
+                                                nrows, ntile, lds, wave, lane, 0);
 }
 
 template <int N, int MB, int NW, int RG, int S, bool SWIGLU>
@@ -396,19 +390,6 @@ int ffn_fp8_choose_mb(int64_t rows, int E) {
   return 12;
 }
 
-// Pipeline shapes (row groups, stages) of the 128- and 192-row configurations.
-#ifndef BEAM_FP8_RG8
-#define BEAM_FP8_RG8 2
-#endif
-#ifndef BEAM_FP8_S8
-#define BEAM_FP8_S8 3
-#endif
-#ifndef BEAM_FP8_RG12
-#define BEAM_FP8_RG12 2
-#endif
-#ifndef BEAM_FP8_S12
-#define BEAM_FP8_S12 3
-#endif
 
 hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                    int topk, const uint8_t* Q, const float* scales, int64_t qstride,
@@ -424,8 +405,10 @@ hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const
                                                            up_row0, max_items, stream);
   switch (mb) {
     BEAM_FP8_CASE(2, 4, 1, 4)
-    BEAM_FP8_CASE(8, 8, BEAM_FP8_RG8, BEAM_FP8_S8)
-    BEAM_FP8_CASE(12, 8, BEAM_FP8_RG12, BEAM_FP8_S12)
+    case 8:
+    case 12:
+      return launch_grouped_gemm_fp8_paired(mb, swiglu, A, gather, topk, Q, scales, qstride, N, C,
+                                            plan, max_tiles, K, n_out, up_row0, max_items, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -49,6 +49,13 @@ hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const
                                    int topk, const uint8_t* Q, const float* scales, int64_t qstride,
                                    int N, uint16_t* C, const int32_t* plan, int max_tiles, int K,
                                    int n_out, int up_row0, int64_t max_items, hipStream_t stream);
+// 128/192-row tiles (mb 8 or 12) of the fp8 path, run by the bf16 kernel's
+// 64-k stage pipeline (ffn.hip)
+hipError_t launch_grouped_gemm_fp8_paired(int mb, bool swiglu, const uint16_t* A,
+                                          const int32_t* gather, int topk, const uint8_t* Q,
+                                          const float* scales, int64_t qstride, int N, uint16_t* C,
+                                          const int32_t* plan, int max_tiles, int K, int n_out,
+                                          int up_row0, int64_t max_items, hipStream_t stream);
 hipError_t launch_quantize_fp8(const uint16_t* w, uint8_t* q, float* scales, int E, int N, int K,
                                hipStream_t stream);
 

@@ -214,9 +214,9 @@ int moe_pack_weights(const moe_config_t* cfg, const uint16_t* w_gate_up, const u
  * router, selection, permutation and combine are the bf16 path's.
  *
  * Code layout (MOE_LAYOUT_FP8_PACKED): each expert's [N, K] code matrix is
- * stored as [N/16][K/64][64][16] bytes; entry (b, s, l) holds row
- * 16b + l%16, bytes 0..7 at k = 64s + 8(l/16) .. +7 and bytes 8..15 at
- * k = 64s + 32 + 8(l/16) .. +7.  Scales are plain fp32 [E, N].
+ * stored as [N/16][K/64][2][64][8] bytes; entry (b, s, h, l) holds the codes
+ * of row 16b + l%16 at k = 64s + 32h + 8(l/16) .. +7.  Scales are plain
+ * fp32 [E, N].
  *   q_gate_up [E, 2*I, H] codes, s_gate_up [E, 2*I]
  *   q_down    [E, H, I]   codes, s_down    [E, H]
  * The *_fp8 calls require cfg->weight_layout == MOE_LAYOUT_FP8_PACKED (else

@@ -93,13 +93,12 @@ def layer_reference(ids_gpu, ref, x, experts, *, renormalize=True, scale=2.5):
 
 def unpack_fp8_codes(q):
     """Row-major [E, N, K] codes from the library's fp8 fragment layout
-    ([N/16][K/64][64 lanes][16 bytes] per expert; lane l = r + 16g holds row
-    16b + r, bytes 0..7 at k = 64s + 8g + j and bytes 8..15 at
-    k = 64s + 32 + 8g + j)."""
+    ([N/16][K/64][2][64 lanes][8 bytes] per expert; entry (b, s, h, l) with
+    l = r + 16g holds row 16b + r at k = 64s + 32h + 8g + j, j = 0..7)."""
     q = np.asarray(q, dtype=np.uint8)
     E, N, K = q.shape
-    p = q.reshape(E, N // 16, K // 64, 4, 16, 2, 8)        # e, b, s, g, r, h, j
-    return p.transpose(0, 1, 4, 2, 5, 3, 6).reshape(E, N, K)  # e, b, r, s, h, g, j
+    p = q.reshape(E, N // 16, K // 64, 2, 4, 16, 8)        # e, b, s, h, g, r, j
+    return p.transpose(0, 1, 5, 2, 3, 4, 6).reshape(E, N, K)  # e, b, r, s, h, g, j
 
 
 class OracleFp8Experts:
