@@ -283,6 +283,24 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     }
   };
 
+  // paired: issue the weights of 64-k stage P into slot P % S
+  auto issue_b64 = [&](const uint8_t* const (&src)[NBL], int P) {
+    const uint32_t so = (uint32_t)((P % S) * BSTAGE);
+    if constexpr (F8) {
+#pragma unroll
+      for (int t = 0; t < NBL; ++t)
+        lds_dma16_sv<kStreamWeights>(src[t] + (size_t)P * kFrag, boff,
+                                     b_base + so + RG * t * kFrag);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < NBL; ++t)
+          lds_dma16_sv<kStreamWeights>(src[t] + (size_t)(2 * P + h) * bstep, boff,
+                                       b_base + so + h * BSUB + RG * t * kFrag);
+    }
+  };
+
   if constexpr (kPairA) {
     // ---- 128/192-row tiles: 64-k stages ----
     // Stage P: weights of sub-steps 2P, 2P+1 in slot P % S (issued S - 1
@@ -295,22 +313,6 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     // weight loads of one stage per wave: bf16 two 1 KB fragments (32 k
     // each) per column block it loads, fp8 one (64 k)
     constexpr int kStageLoads = F8 ? NBL : 2 * NBL;
-    auto issue_b64 = [&](const uint8_t* const (&src)[NBL], int P) {
-      const uint32_t so = (uint32_t)((P % S) * BSTAGE);
-      if constexpr (F8) {
-#pragma unroll
-        for (int t = 0; t < NBL; ++t)
-          lds_dma16_sv<kStreamWeights>(src[t] + (size_t)P * kFrag, boff,
-                                       b_base + so + RG * t * kFrag);
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int t = 0; t < NBL; ++t)
-            lds_dma16_sv<kStreamWeights>(src[t] + (size_t)(2 * P + h) * bstep, boff,
-                                         b_base + so + h * BSUB + RG * t * kFrag);
-      }
-    };
     auto issue_a64 = [&](int P) {
       const uint32_t po = (uint32_t)((P & 1) * APAIR);
       const int k0 = P * 2 * kBKS;
@@ -393,18 +395,6 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
         for (int cb = 0; cb < NCBW; ++cb) acc[i][cb] *= wscale[cb];
     }
 
-    // Start the next item's weight stream now (stage slots 0..kPre-1); the
-    // epilogue below works in the LDS past them.
-    const int qn = a.q + a.grid;
-    if (kPre > 0 && qn < a.total) {
-      const int tn = qn / a.nt_n;
-      const uint16_t* nw = a.W0 + (size_t)a.plan_expert[tn] * a.w_expert_stride;
-      const uint8_t* nsrc[NBL];
-#pragma unroll
-      for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
-#pragma unroll
-      for (int P = 0; P < kPre; ++P) issue_b64(nsrc, P);
-    }
   } else {
     // ---- 64-row tiles: 32-k stages, B and A of a stage in one slot ----
     auto issue = [&](int st) {
@@ -491,6 +481,21 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
                                                                  acc[i][cb], 0, 0, 0);
         }
       }
+    }
+  }
+
+  // Paired: start the next item's weight stream now (stage slots
+  // 0..kPre-1); the epilogue below works in the LDS past them.
+  if constexpr (kPairA) {
+    const int qn = a.q + a.grid;
+    if (kPre > 0 && qn < a.total) {
+      const int tn = qn / a.nt_n;
+      const uint16_t* nw = a.W0 + (size_t)a.plan_expert[tn] * a.w_expert_stride;
+      const uint8_t* nsrc[NBL];
+#pragma unroll
+      for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
+#pragma unroll
+      for (int P = 0; P < kPre; ++P) issue_b64(nsrc, P);
     }
   }
 
