@@ -43,6 +43,8 @@
 // * Wave-level values (wave index, wait counts, weight row bases) are kept in
 //   scalar registers: every weight load takes a 64-bit base in SGPRs and one
 //   32-bit lane offset, and the run-time vmcnt waits branch on scalars.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -695,15 +697,23 @@ static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int to
     cus = n;
     per_cu = occ > 0 ? occ : 1;
   }
-  int64_t grid = (int64_t)cus * per_cu;
-  const int64_t cap = (max_items + 7) / 8 * 8;
-  if (cap < grid) grid = cap;
-  grid = (grid + 7) / 8 * 8;
-  if (grid < 8) grid = 8;
+  const int64_t grid = persistent_grid((int64_t)cus * per_cu, max_items);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, stream, A, gather, topk, W,
                      wstride, C, plan, max_tiles, K, n_out, up_row0, packed, lora.t, lora.b,
                      lora.b_stride, lora.rank, scales, scale_stride);
   return hipGetLastError();
+}
+
+int64_t persistent_grid(int64_t resident, int64_t max_items) {
+  int64_t grid = resident;
+  const int64_t cap = (max_items + 7) / 8 * 8;
+  if (cap < grid) grid = cap;
+  if (const char* env = getenv("BEAM_MOE_MAX_GRID")) {
+    const long long m = atoll(env);
+    if (m > 0 && m < grid) grid = m;
+  }
+  grid = (grid + 7) / 8 * 8;
+  return grid < 8 ? 8 : grid;
 }
 
 int ffn_rows_per_tile(int mb) { return 16 * mb; }

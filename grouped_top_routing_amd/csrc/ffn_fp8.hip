@@ -371,11 +371,7 @@ static hipError_t launch_fp8(const uint16_t* A, const int32_t* gather, int topk,
     cus = n;
     per_cu = occ > 0 ? occ : 1;
   }
-  int64_t grid = (int64_t)cus * per_cu;
-  const int64_t cap = (max_items + 7) / 8 * 8;
-  if (cap < grid) grid = cap;
-  grid = (grid + 7) / 8 * 8;
-  if (grid < 8) grid = 8;
+  const int64_t grid = persistent_grid((int64_t)cus * per_cu, max_items);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, stream, A, gather, topk, Q,
                      scales, qstride, N, C, plan, max_tiles, K, n_out, up_row0);
   return hipGetLastError();

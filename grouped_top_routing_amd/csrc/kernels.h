@@ -8,6 +8,13 @@ namespace beam {
 
 constexpr int kChunk = 4096;  // (token, slot) pairs per permute workgroup
 
+// Workgroups of a persistent grouped-GEMM launch: `resident` (one per
+// resident slot on the device) capped by the item count, a multiple of 8
+// (one per XCD), at least 8.  BEAM_MOE_MAX_GRID=<n> in the environment caps
+// it further (results do not depend on the grid; tests use it to run many
+// items per workgroup).
+int64_t persistent_grid(int64_t resident, int64_t max_items);
+
 int router_splits(int64_t T, int H);
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H,
                                 int splits, hipStream_t stream);

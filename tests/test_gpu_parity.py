@@ -320,3 +320,36 @@ def test_layer_replays_from_a_captured_graph(tiny, variant):
         want = call(x)          # eager work between the replays
         torch.cuda.synchronize()
         assert torch.equal(got, want), f"replay {rep} differs from the eager call"
+
+
+# -------------------------------------------------------- grid independence
+@pytest.mark.parametrize("variant,T", [("bf16", 128), ("bf16", 2048), ("bf16", 4096),
+                                       ("fp8", 64), ("fp8", 2048), ("fp8", 4096),
+                                       ("lora", 4096)])
+def test_layer_independent_of_grid_size(tiny, variant, T, monkeypatch):
+    # each work item is computed whole by one workgroup, so capping the
+    # persistent GEMM grid must not change a bit; with 8 workgroups every
+    # workgroup runs a long chain of items (each starting the next one's
+    # weight stream early) at every m-tile height (T 64..128 -> 32/64 rows,
+    # 2048 -> 128, 4096 -> 192)
+    say(f"[grid] {variant} T={T}")
+    wr, wgu, wd = tiny["w_router"], tiny["w_gate_up"], tiny["w_down"]
+    f8 = gtr.quantize_fp8(wgu, wd) if variant == "fp8" else None
+    lw = (gtr.LoraWeights(*synth.make_lora(tiny["workload"], 0, DEV), scale=2.0)
+          if variant == "lora" else None)
+    x = synth.make_x(synth.workload("tiny", T=T), 11, DEV)
+
+    def call():
+        if variant == "fp8":
+            return gtr.layer_forward_fp8(x, wr, f8)
+        if variant == "lora":
+            return gtr.layer_forward_lora(x, wr, wgu, wd, lw)
+        return gtr.layer_forward(x, wr, wgu, wd)
+
+    ref = call()
+    for cap in ("8", "24", "200"):
+        monkeypatch.setenv("BEAM_MOE_MAX_GRID", cap)
+        out = call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"grid cap {cap} changes the result"
+    monkeypatch.delenv("BEAM_MOE_MAX_GRID")
