@@ -5,9 +5,11 @@
 // normalized router weights and scaled by 2.5; there is no shared expert.
 //
 // out[t, :] = bf16( scale * sum_j w[t, j] * y[perm_dst[t*topk + j], :] ), the
-// sum taken in fp32 in slot order.  One workgroup per token; every thread
-// owns 8 consecutive columns, so each of the token's rows is read with
-// coalesced 16-byte loads and the output row is written the same way.
+// sum taken in fp32 in slot order.  Workgroup (t, c) handles token t's c-th
+// slice of columns (one slice for large batches; small batches split each
+// row so that enough workgroups run); every thread owns 8 consecutive
+// columns, so each of the token's rows is read with coalesced 16-byte loads
+// and the output row is written the same way.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,6 +21,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
                                                       uint16_t* __restrict__ out, int H, int topk,
                                                       float scale) {
   const int t = blockIdx.x;
+  const int per = (H / 8 + gridDim.y - 1) / gridDim.y;  // 16-byte column groups per slice
+  const int v0 = blockIdx.y * per, v1 = min(v0 + per, H / 8);
   int rows[8];
   float wt[8];
 #pragma unroll
@@ -26,7 +30,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
     rows[j] = j < topk ? perm_dst[(size_t)t * topk + j] : -1;
     wt[j] = j < topk ? w[(size_t)t * topk + j] : 0.f;
   }
-  for (int v = threadIdx.x; v < H / 8; v += blockDim.x) {
+  for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -50,8 +54,14 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
                           uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(128), 0, stream, y, perm_dst, w, out, H, topk,
-                     scale);
+  // slices of at least 128 column groups, enough of them for ~1024 workgroups
+  const int groups = H / 8;
+  int slices = (1024 + T - 1) / (T > 0 ? T : 1);
+  const int max_slices = (groups + 127) / 128;
+  if (slices > max_slices) slices = max_slices;
+  if (slices < 1) slices = 1;
+  hipLaunchKernelGGL(combine_kernel, dim3(T, slices), dim3(128), 0, stream, y, perm_dst, w, out, H,
+                     topk, scale);
   return hipGetLastError();
 }
 
