@@ -6,7 +6,7 @@
 
 namespace beam {
 
-constexpr int kChunk = 4096;  // (token, slot) pairs per permute workgroup
+constexpr int kChunk = 1024;  // (token, slot) pairs per permute workgroup
 
 // Workgroups of a persistent grouped-GEMM launch: `resident` (one per
 // resident slot on the device) capped by the item count, a multiple of 8

@@ -79,10 +79,16 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = total;
-      total += v;
+    // running total over chunks, 8 chunks' loads in flight at a time
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = c0 + j < nchunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (c0 + j < nchunks) chunk_hist[(size_t)(c0 + j) * E + e] = total;
+        total += v[j];
+      }
     }
   }
   sc[e] = e < E ? total : 0;
@@ -98,7 +104,14 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
   if (e < E) {
     counts[e] = total;
     offsets[e] = excl;
-    for (int c = 0; c < nchunks; ++c) chunk_hist[(size_t)c * E + e] += excl;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = c0 + j < nchunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < nchunks) chunk_hist[(size_t)(c0 + j) * E + e] = v[j] + excl;
+    }
   }
   if (e == E - 1) offsets[E] = excl + total;
 }
