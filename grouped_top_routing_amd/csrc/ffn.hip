@@ -143,13 +143,6 @@ constexpr int ring_bytes() {
   return pair_a<MB>() ? S * (F8 ? 1 : 2) * kItemBlocks * kFrag + 2 * MB * 2 * kFrag
                       : S * (kItemBlocks + MB) * kFrag;
 }
-// LDS of one workgroup: the ring, or the largest epilogue tile (16 * MB rows
-// of the item's columns plus 8 bf16 of padding) if that is larger.
-template <int MB, int S, bool SWIGLU, bool F8 = false>
-constexpr int lds_bytes() {
-  constexpr int tile = 16 * MB * ((SWIGLU ? kColsGateUp : kColsDown) + 8) * 2;
-  return ring_bytes<MB, S, F8>() > tile ? ring_bytes<MB, S, F8>() : tile;
-}
 
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
 // this wave computes RB blocks starting at block row_off.  MB sizes the LDS
@@ -173,13 +166,10 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
   constexpr int WCOLS = CG * HALF * 16;
   constexpr int RBX = RB > 0 ? RB : 1;
-  constexpr int TSTRIDE = WCOLS + 8;  // bf16 elements per epilogue tile row
   // Paired: weight stages of the workgroup's next item issued while this
-  // item's epilogue runs -- as many as fit below the largest epilogue tile,
-  // and at most S - 2 (the prologue issues stage S - 1 after the first A).
-  constexpr int kPre = kPairA ? std::min(S - 2, (lds_bytes<MB, S, SWIGLU, F8>() - 16 * MB * TSTRIDE * 2) /
-                                                    BSTAGE)
-                              : 0;
+  // item's epilogue runs: S - 2 (the prologue issues stage S - 1 after the
+  // first A stages).
+  constexpr int kPre = kPairA ? S - 2 : 0;
   // Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
   // weight stream: weights are then loaded with the non-temporal policy,
   // which measured 6.6 TB/s against 6.1 TB/s with the default one.  The
@@ -244,12 +234,14 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 #pragma unroll
   for (int t = 0; t < NBL; ++t) bsrc[t] = bbase_of(a.W, a.ntile, t);
   const int bstep = a.packed ? kFrag : kBKS * 2;  // bf16: bytes per 32-k stage along a stream
-  // fp8: the fp32 scale of each of this lane's weight-row columns, applied
-  // to the accumulators after the k loop
-  float wscale[F8 ? NCBW : 1];
+  // fp8: the fp32 scales of this lane's four output columns (weight rows
+  // 4g..4g+3 of each column block), applied to the accumulators after the k
+  // loop
+  f32x4_t wscale[F8 ? NCBW : 1];
   if constexpr (F8) {
 #pragma unroll
-    for (int cb = 0; cb < NCBW; ++cb) wscale[cb] = a.scale[weight_row(cb)];
+    for (int cb = 0; cb < NCBW; ++cb)
+      wscale[cb] = *reinterpret_cast<const f32x4_t*>(a.scale + weight_row(cb) - r + 4 * g);
   }
   // LDS byte offset of the ring (addrspace cast, not the flat address)
   const uint32_t lds0 =
@@ -279,7 +271,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 #pragma unroll
         for (int cb = 0; cb < NCBW; ++cb)
           acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(af[i]), as_bf16x8(cbf[cb]), acc[i][cb], 0, 0, 0);
+              as_bf16x8(cbf[cb]), as_bf16x8(af[i]), acc[i][cb], 0, 0, 0);
         if (more) af[i] = next_a(i);
       }
     }
@@ -479,7 +471,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
           const uint4 al = live ? ld16(a.lora_t + (size_t)(a.row0 + row) * R + k0 + 8 * g) : zero;
 #pragma unroll
           for (int cb = 0; cb < NCBW; ++cb)
-            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bl[cb]),
+            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bl[cb]), as_bf16x8(al),
                                                                  acc[i][cb], 0, 0, 0);
         }
       }
@@ -487,7 +479,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   }
 
   // Paired: start the next item's weight stream now (stage slots
-  // 0..kPre-1); the epilogue below works in the LDS past them.
+  // 0..kPre-1), before this item's epilogue, which needs no LDS.
   if constexpr (kPairA) {
     const int qn = a.q + a.grid;
     if (kPre > 0 && qn < a.total) {
@@ -501,52 +493,39 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     }
   }
 
-  // Epilogue through LDS (the ring is free after the barrier above): each
-  // wave writes its accumulators as bf16 into a row-major tile -- lane holds
-  // rows 4g..4g+3 of column r of each 16x16 block; even lanes pair up with
-  // their right neighbour for 4-byte writes -- then every thread stores whole
-  // 16-byte row segments, so each output row leaves as 256 or 512 contiguous
-  // bytes.  Rows are padded by 16 bytes so the 4 row groups of a write land
-  // on different LDS banks.
-  constexpr int TILE0 = kPre * BSTAGE;  // past the next item's weight stages
-  static_assert(TILE0 + 16 * NRB * TSTRIDE * 2 <= lds_bytes<MB, S, SWIGLU, F8>(), "epilogue tile fits");
-  uint16_t* tile = reinterpret_cast<uint16_t*>(lds + TILE0);
+  // Epilogue straight from the accumulators.  The MFMAs take the weights as
+  // their first operand, so each 16x16 accumulator block is the transposed
+  // output tile: lane (r, g) holds output columns 4g..4g+3 of row r, which
+  // leave as one 8-byte store (four bf16); the column blocks of one row are
+  // written by neighbouring lanes and waves in the same few instructions and
+  // merge into whole lines in L2.
   if constexpr (RB > 0) {
+    uint16_t* out = a.C + (size_t)a.row0 * a.n_out + a.ntile * WCOLS;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
+      const int row = (row_off + i) * 16 + r;
+      if (row < a.nrows) {
 #pragma unroll
-      for (int j = 0; j < HALF; ++j) {
-        const int col = cg * HALF * 16 + j * 16 + r;
+        for (int j = 0; j < HALF; ++j) {
+          uint32_t h[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = (row_off + i) * 16 + 4 * g + v;
-          float o;
-          if (SWIGLU) {
-            const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
-            o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
-          } else {
-            o = acc[i][j][v];
+          for (int v = 0; v < 4; ++v) {
+            float o;
+            if (SWIGLU) {
+              const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
+              o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+            } else {
+              o = acc[i][j][v];
+            }
+            h[v] = f32_to_bf16(o);
           }
-          const uint32_t b = f32_to_bf16(o);
-          const uint32_t nb = __shfl_xor(b, 1);
-          if ((r & 1) == 0)
-            *reinterpret_cast<uint32_t*>(tile + row * TSTRIDE + col) = b | (nb << 16);
+          const int col = cg * HALF * 16 + j * 16 + 4 * g;
+          *reinterpret_cast<uint2*>(out + (size_t)row * a.n_out + col) =
+              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
       }
     }
   }
-  wait_lgkm0();
-  stage_barrier();
-  constexpr int CPR = WCOLS / 8;  // 16-byte chunks per tile row
-  const int nchunks = a.nrows * CPR;
-  uint16_t* out = a.C + (size_t)a.row0 * a.n_out + a.ntile * WCOLS;
-  for (int c = wave * 64 + lane; c < nchunks; c += kNW * 64) {
-    const int row = c / CPR, cc = c - row * CPR;
-    st16(out + (size_t)row * a.n_out + cc * 8,
-         *reinterpret_cast<const uint4*>(tile + row * TSTRIDE + cc * 8));
-  }
-  wait_lgkm0();
-  stage_barrier();  // the tile is read out before the next item refills the ring
 }
 
 // Item with NRB live row blocks: row group 0 takes the first ceil(NRB / RG)
@@ -585,7 +564,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     int64_t lora_b_stride, int lora_r, const float* __restrict__ scales, int64_t scale_stride) {
   constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<MB, S, SWIGLU, F8>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring_bytes<MB, S, F8>()];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
