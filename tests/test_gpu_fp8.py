@@ -110,11 +110,12 @@ def test_expert_ffn_fp8(tiny):
 
 
 @pytest.mark.parametrize("hot_rows,T", [(1, 64), (17, 64), (40, 700), (130, 700), (300, 1024),
-                                        (1000, 3072)])
+                                        (1000, 3072), (3000, 16384)])
 def test_expert_ffn_fp8_ragged_tiles(tiny, hot_rows, T):
     # one hot expert plus thin ones: ragged m-tiles at every tile height the
     # fp8 path picks (mean rows per expert 2 and 21 -> 32-row tiles, 32 ->
-    # 128 rows, 96 -> 192 rows)
+    # 128 rows, 96 and 512 -> 192 rows; at 16384 tokens each workgroup runs
+    # several items back to back)
     say(f"[fp8] expert_ffn ragged hot_rows={hot_rows} T={T}")
     rng = np.random.default_rng(hot_rows + 1)
     ids = np.stack([rng.choice(np.arange(1, 256), 8, replace=False) for _ in range(T)])
