@@ -76,7 +76,7 @@ namespace beam {
 #ifndef BEAM_GEMM_RG12
 #define BEAM_GEMM_RG12 2
 #endif
-constexpr int kBKS = 32;                // k per pipeline stage (one MFMA k)
+constexpr int kBKS = 32;                // k per MFMA step (a 64-row tile's pipeline stage)
 constexpr int kFrag = 1024;             // bytes of one 16 x 32 bf16 MFMA operand
 constexpr int kFragElems = kFrag / 2;
 // Output columns of one work item: every configuration covers 128 h columns
@@ -132,9 +132,10 @@ constexpr int kItemBlocks = 16;
 // holds 2 KB, rows 0-7 then rows 8-15, each row's 128 bytes with its 16-byte
 // chunks XOR-swizzled by (row / 2) % 8 so that the MFMA operand reads (16
 // rows at one logical chunk) hit distinct LDS banks.  Weights then have a
-// ring of S stage slots of 2 x 16 KB, issued S - 1 stages ahead, and A a ring
-// of two slots issued one stage ahead (A comes from L2; the weights from HBM
-// need the deeper look-ahead).
+// ring of S stage slots of 2 x 16 KB (fp8: 16 KB), issued S - 1 stages
+// ahead, and A a ring of two slots issued one stage ahead (A comes from L2;
+// the weights from HBM need the deeper look-ahead).  Below, "paired" names
+// this 128/192-row family (A staged two MFMA k-steps at a time).
 template <int MB>
 constexpr bool pair_a() { return MB >= 8; }
 __device__ __forceinline__ int a_swizzle(int row) { return (row >> 1) & 7; }
@@ -249,9 +250,9 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds0 + (cg * NCBW + rg) * kFrag);
   const uint32_t a_base = __builtin_amdgcn_readfirstlane(
       kPairA ? lds0 + APOFF + wave * 2 * kFrag : lds0 + AOFF + wave * kFrag);
-  // byte offset, inside a pair's 2 KB row block, of this lane's MFMA operand
-  // (row r, logical chunk g) for the pair's first stage; the second stage
-  // reads logical chunk 4 + g, the same address with bit 6 flipped
+  // byte offset, inside a 64-k stage's 2 KB row block, of this lane's MFMA
+  // operand (row r, logical chunk g) for the stage's first 32-k sub-step; the
+  // second reads logical chunk 4 + g, the same address with bit 6 flipped
   const int aoff0 = (r >> 3) * kFrag + (r & 7) * 128 + ((g ^ a_swizzle(r)) << 4);
 
   f32x4_t acc[RBX][NCBW];
