@@ -23,8 +23,10 @@ namespace {
 
 constexpr int kK = 32;  // k per MFMA
 
+constexpr int kLoraWaves = 8;  // waves per workgroup, each on its own 16-row blocks
+
 template <int RB>
-__global__ __launch_bounds__(256) void lora_a_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(kLoraWaves * 64) void lora_a_kernel(const uint16_t* __restrict__ X,
                                                      const int32_t* __restrict__ gather, int topk,
                                                      const uint16_t* __restrict__ La, int K,
                                                      float scale, uint16_t* __restrict__ t,
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void lora_a_kernel(const uint16_t* __restrict_
   const int r = lane & 15, g = lane >> 4;
   const uint16_t* La_e = La + (size_t)e * R * K;
   const int nblk = (nrows + 15) >> 4;
-  for (int b = wave; b < nblk; b += 4) {
+  for (int b = wave; b < nblk; b += kLoraWaves) {
     int row = b * 16 + r;
     row = row < nrows ? row : nrows - 1;
     const int src = gather ? gather[row0 + row] / topk : row0 + row;
@@ -50,17 +52,29 @@ __global__ __launch_bounds__(256) void lora_a_kernel(const uint16_t* __restrict_
     f32x4_t acc[RB];
 #pragma unroll
     for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // K is a multiple of 128 (hidden % 256 == 0, intermediate % 128 == 0)
-    for (int k0 = 0; k0 < K; k0 += 4 * kK) {
+    // K is a multiple of 128 (hidden % 256 == 0, intermediate % 128 == 0):
+    // 8 k-steps per group when K allows (all their loads issued before the
+    // first MFMA), else 4
+    auto group = [&](int k0, auto steps) {
+      constexpr int U = decltype(steps)::value;
+      uint4 av[U], bv[U][RB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = k0 + u * kK;
-        const bf16x8_t a = as_bf16x8(ld16(ap + k));
+      for (int u = 0; u < U; ++u) {
+        av[u] = ld16(ap + k0 + u * kK);
+#pragma unroll
+        for (int j = 0; j < RB; ++j) bv[u][j] = ld16(bp + (size_t)j * 16 * K + k0 + u * kK);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a, as_bf16x8(ld16(bp + (size_t)j * 16 * K + k)), acc[j], 0, 0, 0);
-      }
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][j]),
+                                                           acc[j], 0, 0, 0);
+    };
+    if (K % (8 * kK) == 0) {
+      for (int k0 = 0; k0 < K; k0 += 8 * kK) group(k0, std::integral_constant<int, 8>{});
+    } else {
+      for (int k0 = 0; k0 < K; k0 += 4 * kK) group(k0, std::integral_constant<int, 4>{});
     }
     // lane holds rows 4g..4g+3 of rank column j*16 + r
 #pragma unroll
@@ -80,7 +94,7 @@ __global__ __launch_bounds__(256) void lora_a_kernel(const uint16_t* __restrict_
 hipError_t launch_lora_a(const uint16_t* X, const int32_t* gather, int topk, const uint16_t* La,
                          int K, int rank, float scale, uint16_t* t, const int32_t* plan,
                          int max_tiles, hipStream_t stream) {
-  const dim3 grid((unsigned)max_tiles), block(256);
+  const dim3 grid((unsigned)max_tiles), block(kLoraWaves * 64);
   switch (rank) {
     case 16:
       hipLaunchKernelGGL(lora_a_kernel<1>, grid, block, 0, stream, X, gather, topk, La, K, scale,
