@@ -35,16 +35,19 @@ namespace beam {
 //
 // Tile: 128 tokens x 256 experts per workgroup, k split over blockIdx.y (the
 // partial sums are added in split order by select_kernel, so results do not
-// depend on the grid).  Wave w owns experts [64w, 64w + 64) and all 128
-// tokens.  x fragments (16 tokens x 32 k, MFMA lane order) stream into an LDS
-// ring with direct loads shared by the 4 waves; each wave's weights go
-// straight to registers (no other wave needs them), both kRD stages ahead.
+// depend on the grid).  Wave w of 8 owns experts [32w, 32w + 32) and all 128
+// tokens (two waves per SIMD).  x fragments (16 tokens x 32 k, MFMA lane
+// order) stream into an LDS ring with direct loads shared by the 8 waves;
+// each wave's weights go straight to registers (no other wave needs them),
+// both kRD stages ahead.
 // ---------------------------------------------------------------------------
 constexpr int kRT = 128;              // tokens per workgroup
 constexpr int kRB = kRT / 16;         // token row blocks
 constexpr int kRD = 3;                // stages in flight
 constexpr int kRS = kRD + 1;          // LDS ring slots
-constexpr int kRL = 2 + 8;            // loads per wave per stage: 2 x fragments + 4 experts x 32 B
+constexpr int kRW = 8;                // waves per workgroup
+constexpr int kRC = 256 / kRW / 16;   // 16-expert column blocks per wave
+constexpr int kRL = kRB / kRW + 2 * kRC;  // loads per wave per stage: x fragments + weight halves
 
 __device__ __forceinline__ uint32_t hi16(uint32_t u) { return u & 0xffff0000u; }
 
@@ -69,7 +72,7 @@ __device__ __forceinline__ void split3(const uint4& w0, const uint4& w1, bf16x8_
   pl = as_bf16x8(L);
 }
 
-__global__ __launch_bounds__(256, 1) void router_logits_kernel(
+__global__ __launch_bounds__(kRW * 64, 1) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ part,
     int T, int H, int kchunk) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kRS * kRB * 1024];
@@ -79,55 +82,57 @@ __global__ __launch_bounds__(256, 1) void router_logits_kernel(
   const int kbeg = blockIdx.y * kchunk;
   const int nk = kchunk / 32;
 
-  // x fragments this wave loads: row blocks wave and wave + 4
-  const uint16_t* xsrc[2];
+  // x fragments this wave loads: row blocks wave, wave + kRW, ...
+  constexpr int XJ = kRB / kRW;
+  const uint16_t* xsrc[XJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int t = t0 + (wave + 4 * j) * 16 + r;
+  for (int j = 0; j < XJ; ++j) {
+    int t = t0 + (wave + kRW * j) * 16 + r;
     t = t < T ? t : T - 1;  // rows past T repeat the last token (computed, never stored)
     xsrc[j] = x + (size_t)t * H + kbeg + 8 * g;
   }
-  // weight rows of this lane: expert 64*wave + 16*cb + r, k chunk 8g
-  const float* wsrc[4];
+  // weight rows of this lane: expert 16 * (kRC * wave + cb) + r, k chunk 8g
+  const float* wsrc[kRC];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) wsrc[cb] = wr + (size_t)(64 * wave + 16 * cb + r) * H + kbeg + 8 * g;
+  for (int cb = 0; cb < kRC; ++cb)
+    wsrc[cb] = wr + (size_t)(16 * (kRC * wave + cb) + r) * H + kbeg + 8 * g;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
-  uint4 wreg[kRD][4][2];
-  auto issue = [&](int st, uint4 (&wr_)[4][2]) {
+  uint4 wreg[kRD][kRC][2];
+  auto issue = [&](int st, uint4 (&wr_)[kRC][2]) {
     const uint32_t sl = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((st % kRS) * kRB * 1024));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(xsrc[j] + st * 32, sl + (wave + 4 * j) * 1024);
+    for (int j = 0; j < XJ; ++j) lds_dma16(xsrc[j] + st * 32, sl + (wave + kRW * j) * 1024);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kRC; ++cb) {
       wr_[cb][0] = ld16(wsrc[cb] + st * 32);
       wr_[cb][1] = ld16(wsrc[cb] + st * 32 + 4);
     }
   };
 
-  f32x4_t acc[kRB][4];
+  f32x4_t acc[kRB][kRC];
 #pragma unroll
   for (int i = 0; i < kRB; ++i)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < kRC; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int st = 0; st < kRD; ++st)
     if (st < nk) issue(st, wreg[st]);
 
   // one stage: consume register set `cur`, then refill it with stage kt + kRD
-  auto step = [&](int kt, uint4 (&cur)[4][2]) {
+  auto step = [&](int kt, uint4 (&cur)[kRC][2]) {
     wait_stage<kRD - 1, kRL>(min(kRD - 1, nk - 1 - kt));
     stage_barrier();
     const uint8_t* sl = lds + (kt % kRS) * kRB * 1024;
-    bf16x8_t bh[4], bm[4], bl[4];
+    bf16x8_t bh[kRC], bm[kRC], bl[kRC];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) split3(cur[cb][0], cur[cb][1], bh[cb], bm[cb], bl[cb]);
+    for (int cb = 0; cb < kRC; ++cb) split3(cur[cb][0], cur[cb][1], bh[cb], bm[cb], bl[cb]);
 #pragma unroll
     for (int i = 0; i < kRB; ++i) {
       const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(sl + i * 1024 + 16 * lane));
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < kRC; ++cb) {
         acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[cb], acc[i][cb], 0, 0, 0);
         acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[cb], acc[i][cb], 0, 0, 0);
         acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[cb], acc[i][cb], 0, 0, 0);
@@ -154,7 +159,8 @@ __global__ __launch_bounds__(256, 1) void router_logits_kernel(
       const int t = t0 + i * 16 + 4 * g + v;
       if (t < T) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) out[(size_t)t * 256 + 64 * wave + 16 * cb + r] = acc[i][cb][v];
+        for (int cb = 0; cb < kRC; ++cb)
+          out[(size_t)t * 256 + 16 * (kRC * wave + cb) + r] = acc[i][cb][v];
       }
     }
 }
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(256) void replay_kernel(
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H,
                                 int splits, hipStream_t stream) {
   dim3 grid((T + kRT - 1) / kRT, splits);
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, wr, part, T, H,
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRW * 64), 0, stream, x, wr, part, T, H,
                      H / splits);
   return hipGetLastError();
 }
