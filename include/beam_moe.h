@@ -31,7 +31,10 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
  *     the call never synchronises it.  Calls that share a workspace must be
  *     ordered on one stream.
- *   - Results are bitwise deterministic: no floating-point atomics.
+ *   - Results are bitwise deterministic: no floating-point atomics.  They do
+ *     not depend on the number of workgroups of the persistent expert GEMMs
+ *     either; the environment variable BEAM_MOE_MAX_GRID=<n>, read at each
+ *     launch, caps that number (for testing this).
  *   - Supported shapes: num_experts == 256; num_groups a power of two in
  *     [1, 64]; 1 <= topk_groups <= num_groups; 1 <= topk <= 8 and topk not
  *     above the experts in the kept groups; hidden a multiple of 256;
