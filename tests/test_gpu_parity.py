@@ -353,3 +353,33 @@ def test_layer_independent_of_grid_size(tiny, variant, T, monkeypatch):
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"grid cap {cap} changes the result"
     monkeypatch.delenv("BEAM_MOE_MAX_GRID")
+
+
+# ------------------------------------------------- seeded random batch shapes
+@pytest.mark.parametrize("seed", range(6))
+def test_expert_ffn_random_batches(tiny, seed):
+    # random batch sizes and routing skews (one to three hot experts, the rest
+    # uniform) for the bf16 and fp8 expert paths against the oracle; the
+    # sizes land on every m-tile height and on item counts below, near and
+    # above one item per workgroup
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.choice([1, 7, 100, 333, 1024, 2600, 5000, 9000]))
+    p = np.ones(256)
+    p[rng.choice(256, int(rng.integers(1, 4)), replace=False)] = rng.uniform(20, 200)
+    p /= p.sum()
+    ids = np.stack([rng.choice(256, 8, replace=False, p=p) for _ in range(T)])
+    say(f"[random] seed={seed} T={T}")
+    npd = tiny["np"]
+    x = synth.make_x(synth.workload("tiny", T=T), 40 + seed, DEV)
+    xn = to_np(x)
+    counts, offsets, psrc, pdst = oracle.permute(ids, 256)
+    ps = torch.from_numpy(psrc.astype(np.int32)).to(DEV)
+    of = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
+    y = gtr.expert_ffn(x, ps, of, tiny["w_gate_up"], tiny["w_down"])
+    ref = oracle.expert_ffn(xn, psrc, offsets, (npd["w_gate_up"], npd["w_down"]))
+    assert_close(to_np(y), ref, "y_perm")
+    # the fp8 path on the same batch agrees with its bf16 result to fp8 accuracy
+    f8 = gtr.quantize_fp8(tiny["w_gate_up"], tiny["w_down"])
+    y8 = gtr.expert_ffn_fp8(x, ps, of, f8)
+    rel = (y8.float() - y.float()).norm() / y.float().norm()
+    assert float(rel) < 0.1, f"fp8 vs bf16 relative error {float(rel):.3f}"
