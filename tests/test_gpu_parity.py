@@ -383,3 +383,38 @@ def test_expert_ffn_random_batches(tiny, seed):
     y8 = gtr.expert_ffn_fp8(x, ps, of, f8)
     rel = (y8.float() - y.float()).norm() / y.float().norm()
     assert float(rel) < 0.1, f"fp8 vs bf16 relative error {float(rel):.3f}"
+
+
+# ---------------------------------------------------- other supported shapes
+@pytest.mark.parametrize("H,I", [(512, 384), (768, 640)])
+@pytest.mark.parametrize("T", [96, 2048, 4096])
+def test_expert_paths_other_shapes(H, I, T):
+    # hidden and intermediate sizes other than the tiny and Beam ones (I not a
+    # multiple of 256: odd 64-k stage counts, 3 or 5 n-tiles per m-tile) at
+    # every m-tile height, for the bf16 (row-major and packed), fp8 and LoRA
+    # expert paths against the oracle
+    say(f"[shapes] H={H} I={I} T={T}")
+    w = synth.workload("tiny", T=T, H=H, I=I)
+    wgu, wd = synth.make_experts(w, 3, DEV)
+    x = synth.make_x(w, 4, DEV)
+    rng = np.random.default_rng(T + H)
+    ids = np.stack([rng.choice(256, 8, replace=False) for _ in range(T)])
+    counts, offsets, psrc, pdst = oracle.permute(ids, 256)
+    ps = torch.from_numpy(psrc.astype(np.int32)).to(DEV)
+    of = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
+    xn, gn, dn = to_np(x), to_np(wgu), to_np(wd)
+    ref = oracle.expert_ffn(xn, psrc, offsets, (gn, dn))
+    y = gtr.expert_ffn(x, ps, of, wgu, wd)
+    assert_close(to_np(y), ref, "y_perm")
+    pgu, pdn = gtr.pack_weights(wgu, wd)
+    assert torch.equal(gtr.expert_ffn(x, ps, of, pgu, pdn, weight_layout=gtr.LAYOUT_PACKED), y)
+    f8 = gtr.quantize_fp8(wgu, wd)
+    y8 = gtr.expert_ffn_fp8(x, ps, of, f8)
+    rel = (y8.float() - y.float()).norm() / y.float().norm()
+    assert float(rel) < 0.1, f"fp8 vs bf16 relative error {float(rel):.3f}"
+    ts = synth.make_lora(w, 5, DEV)
+    s = oracle.lora_scale(oracle.LORA_ALPHA, oracle.LORA_RANK)
+    yl = gtr.expert_ffn_lora(x, ps, of, wgu, wd, gtr.LoraWeights(*ts, scale=s))
+    refl = oracle.expert_ffn(xn, psrc, offsets, (gn, dn), lora=tuple(to_np(t) for t in ts),
+                             lora_scale_=s)
+    assert_close(to_np(yl), refl, "y_perm lora")
