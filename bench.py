@@ -196,10 +196,14 @@ def cpu_baseline(w, x, wts, n_experts, torch):
     run, expert time is scaled by rows to the whole layer."""
     import numpy as np
     import oracle
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in libs] or [1])
+        if libs:
+            blas = {"library": libs[0].get("internal_api"), "version": libs[0].get("version"),
+                    "threads": libs[0].get("num_threads")}
     except Exception:
         threads = os.cpu_count()
     xn = x.float().cpu().numpy()
@@ -231,7 +235,7 @@ def cpu_baseline(w, x, wts, n_experts, torch):
                        f"({rows} of {w.K * w.T} rows, scaled by rows)")
                       + f": route+permute {t_route:.2f} s, expert MLPs {t_ffn:.2f} s, combine "
                         f"{t_comb:.2f} s; fp64 NumPy/BLAS; host os.cpu_count()={os.cpu_count()}",
-            "sample_seconds": round(t_route + t_ffn + t_comb, 2)}
+            "sample_seconds": round(t_route + t_ffn + t_comb, 2), "blas": blas}
 
 
 def main():
