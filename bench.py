@@ -185,10 +185,10 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
             "device_step_ms": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
             "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
-            "counts": counts.cpu().numpy(), "ids": ids}
+            "counts": counts.cpu().numpy(), "ids": ids, "out": out}
 
 
-def cpu_baseline(w, x, wts, n_experts, torch):
+def cpu_baseline(w, x, wts, n_experts, torch, gpu_out=None, gpu_ids=None):
     """The oracle as it stands, timed on this host's cores: routing and
     permutation of every token, then the SwiGLU MLPs of the first `n_experts`
     experts with all their rows (each expert's weights are copied to the host
@@ -225,7 +225,7 @@ def cpu_baseline(w, x, wts, n_experts, torch):
         t_ffn += time.perf_counter() - t1
         rows += r1 - r0
     t2 = time.perf_counter()
-    oracle.combine(y, pdst, rr.weights, 2.5)
+    ref = oracle.combine(y, pdst, rr.weights, 2.5)
     t_comb = time.perf_counter() - t2
     est = t_route + t_ffn * (w.K * w.T) / max(rows, 1) + t_comb
     whole = rows == w.K * w.T
@@ -235,7 +235,30 @@ def cpu_baseline(w, x, wts, n_experts, torch):
                        f"({rows} of {w.K * w.T} rows, scaled by rows)")
                       + f": route+permute {t_route:.2f} s, expert MLPs {t_ffn:.2f} s, combine "
                         f"{t_comb:.2f} s; fp64 NumPy/BLAS; host os.cpu_count()={os.cpu_count()}",
-            "sample_seconds": round(t_route + t_ffn + t_comb, 2), "blas": blas}
+            "sample_seconds": round(t_route + t_ffn + t_comb, 2), "blas": blas,
+            "parity": _parity(ref, rr, gpu_out, gpu_ids, rows == w.K * w.T, oracle)}
+
+
+def _parity(ref, rr, gpu_out, gpu_ids, whole, oracle):
+    """The timed GPU output against the oracle's, for the same input: routing
+    sets (tokens within the oracle's selection margin may legitimately
+    differ), and row-wise relative L2 error of the layer output over the
+    tokens routed alike."""
+    import numpy as np
+    if gpu_out is None or gpu_ids is None or not whole:
+        return None
+    ids = np.sort(gpu_ids.cpu().numpy().astype(np.int64), axis=1)
+    same = np.all(ids == np.sort(rr.ids, axis=1), axis=1)
+    flagged = rr.margin < oracle.MARGIN_TOL
+    out = gpu_out.float().cpu().numpy().astype(np.float64)
+    num = np.linalg.norm(out - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    rel = (num / den)[same]
+    return {"tokens": int(ids.shape[0]), "routing_sets_differing": int((~same).sum()),
+            "differing_outside_margin": int((~same & ~flagged).sum()),
+            "margin_flagged": int(flagged.sum()),
+            "out_rel_l2_max": float(rel.max()) if rel.size else None,
+            "out_rel_l2_mean": float(rel.mean()) if rel.size else None}
 
 
 def main():
@@ -435,7 +458,8 @@ def main():
         del ad, lw
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, r["x"], wts, args.cpu_experts, torch)
+        result["cpu_baseline"] = cpu_baseline(w, r["x"], wts, args.cpu_experts, torch,
+                                              gpu_out=r["out"], gpu_ids=r["ids"])
     print(json.dumps(result), flush=True)
 
 
