@@ -264,8 +264,8 @@ def _parity(ref, rr, gpu_out, gpu_ids, whole, oracle):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              "the MoE block is not sharded across GPUs here.", file=sys.stderr)
+        print(f"bench.py: the MoE block runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "it is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
