@@ -100,6 +100,19 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   }
 }
 
+// Workgroups a persistent walk over `total` items uses out of a grid of
+// `grid` (a multiple of 8, one per XCD): the fewest, again a multiple of 8,
+// that still finish in the same number of rounds, so that the last round is
+// as full as it can be (e.g. 2940 items on 512 workgroups: 496 do 6 rounds
+// instead of 512 doing 5 or 6).  The others exit at once.
+__device__ __forceinline__ int balanced_grid(int total, int grid) {
+  if (total <= 0) return grid;
+  const int rounds = (total + grid - 1) / grid;
+  const int per = (total + rounds - 1) / rounds;
+  const int eff = (per + 7) / 8 * 8;
+  return eff < grid ? eff : grid;
+}
+
 // Two E4M3FN codes (bytes 0-1 of w, or bytes 2-3 for HI) widened to two bf16
 // values in one 32-bit word, the lower code in the low half.  Exact: every
 // E4M3FN value is a bf16 value.

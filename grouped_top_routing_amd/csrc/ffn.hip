@@ -575,7 +575,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
   const int* plan_rows = plan_row0 + max_tiles;
   const int nt_n = n_out / WCOLS;
   const int total = ntiles * nt_n;
-  const int grid = gridDim.x, per_xcd = grid / 8;
+  const int grid = balanced_grid(total, gridDim.x), per_xcd = grid / 8;
+  if ((int)blockIdx.x >= grid) return;  // whole workgroup: blockIdx is uniform
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
 
   for (int round = 0;; round += grid) {
