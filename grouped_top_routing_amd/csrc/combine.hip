@@ -15,7 +15,7 @@
 
 namespace beam {
 
-__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ perm_dst,
                                                       const float* __restrict__ w,
                                                       uint16_t* __restrict__ out, int H, int topk,
@@ -31,12 +31,17 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
     wt[j] = j < topk ? w[(size_t)t * topk + j] : 0.f;
   }
   for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
+    // all of the token's row loads in flight before the sums (each y row is
+    // read once: non-temporal)
+    uint4 q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      q[j] = rows[j] >= 0 ? ld16_nt(y + (size_t)rows[j] * H + 8 * v) : make_uint4(0u, 0u, 0u, 0u);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (rows[j] >= 0) {
-        const uint4 q = ld16_nt(y + (size_t)rows[j] * H + 8 * v);  // each y row is read once
-        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+        const uint32_t u[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           acc[2 * c] += wt[j] * bf16_to_f32(u[c] & 0xffffu);
@@ -60,8 +65,10 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const floa
   const int max_slices = (groups + 127) / 128;
   if (slices > max_slices) slices = max_slices;
   if (slices < 1) slices = 1;
-  hipLaunchKernelGGL(combine_kernel, dim3(T, slices), dim3(128), 0, stream, y, perm_dst, w, out, H,
-                     topk, scale);
+  // whole rows: 256 threads; row slices: 128
+  const int threads = slices == 1 ? 256 : 128;
+  hipLaunchKernelGGL(combine_kernel, dim3(T, slices), dim3(threads), 0, stream, y, perm_dst, w, out,
+                     H, topk, scale);
   return hipGetLastError();
 }
 
