@@ -79,13 +79,13 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    // running total over chunks, 8 chunks' loads in flight at a time
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {
-      int v[8];
+    // running total over chunks, 32 chunks' loads in flight at a time
+    for (int c0 = 0; c0 < nchunks; c0 += 32) {
+      int v[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = c0 + j < nchunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+      for (int j = 0; j < 32; ++j) v[j] = c0 + j < nchunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 32; ++j) {
         if (c0 + j < nchunks) chunk_hist[(size_t)(c0 + j) * E + e] = total;
         total += v[j];
       }
@@ -104,12 +104,12 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
   if (e < E) {
     counts[e] = total;
     offsets[e] = excl;
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {
-      int v[8];
+    for (int c0 = 0; c0 < nchunks; c0 += 32) {
+      int v[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = c0 + j < nchunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+      for (int j = 0; j < 32; ++j) v[j] = c0 + j < nchunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 32; ++j)
         if (c0 + j < nchunks) chunk_hist[(size_t)(c0 + j) * E + e] = v[j] + excl;
     }
   }
