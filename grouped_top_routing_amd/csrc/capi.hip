@@ -153,7 +153,8 @@ int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
   return hip_status(launch_grouped_gemm(mb_for(c), true, x, psrc, c->topk, wgu,
                                         (int64_t)2 * I * H, h, plan, (int)max_tiles, H, I, I,
                                         c->weight_layout, lora,
-                                        max_tiles * (I / ffn_out_cols_per_item(true)), s));
+                                        max_tiles * (I / ffn_out_cols_per_item(true)), s,
+                                        ffn_stream_weights(pairs(c), c->num_experts)));
 }
 
 int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint16_t* wd,
@@ -163,7 +164,8 @@ int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const
   return hip_status(launch_grouped_gemm(mb_for(c), false, h, nullptr, c->topk, wd,
                                         (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0,
                                         c->weight_layout, lora,
-                                        max_tiles * (H / ffn_out_cols_per_item(false)), s));
+                                        max_tiles * (H / ffn_out_cols_per_item(false)), s,
+                                        false));
 }
 
 int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const int32_t* offsets,

@@ -148,7 +148,7 @@ constexpr int ring_bytes() {
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
 // this wave computes RB blocks starting at block row_off.  MB sizes the LDS
 // ring; fragments of blocks NRB..MB-1 are not loaded.
-template <int NRB, int RB, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
+template <int NRB, int RB, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8, bool NT>
 __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, int wave, int lane,
                                                int row_off) {
   constexpr int CG = kNW / RG;
@@ -171,12 +171,9 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // item's epilogue runs: S - 2 (the prologue issues stage S - 1 after the
   // first A stages).
   constexpr int kPre = kPairA ? S - 2 : 0;
-  // Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
-  // weight stream: weights are then loaded with the non-temporal policy,
-  // which measured 6.6 TB/s against 6.1 TB/s with the default one.  The
-  // 192-row configuration keeps the default (it was 1-20 % slower with
-  // non-temporal loads, most at the skewed batch that re-reads hot experts).
-  constexpr bool kStreamWeights = MB <= 8;
+  // NT: weights are loaded with the non-temporal policy.  The launch picks
+  // it where the kernel is a pure weight stream (see launch_grouped_gemm).
+  constexpr bool kStreamWeights = NT;
   static_assert(CG * RG == kNW && NCBW * CG == kItemBlocks && NBL * RG == NCBW, "work split");
   // A fragments this wave loads: blocks wave, wave + kNW, ... below NRB
   constexpr int AMAX = (NRB + kNW - 1) / kNW;
@@ -531,32 +528,32 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 
 // Item with NRB live row blocks: row group 0 takes the first ceil(NRB / RG)
 // blocks, row group 1 the rest.
-template <int NRB, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
+template <int NRB, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8, bool NT>
 __device__ __forceinline__ void gemm_item(const ItemArgs& a, uint8_t* lds, int wave, int lane) {
   if constexpr (RG == 1) {
-    gemm_item_rows<NRB, NRB, MB, kNW, 1, S, SWIGLU, F8>(a, lds, wave, lane, 0);
+    gemm_item_rows<NRB, NRB, MB, kNW, 1, S, SWIGLU, F8, NT>(a, lds, wave, lane, 0);
   } else {
     static_assert(RG == 2, "one or two row groups");
     constexpr int RB0 = (NRB + 1) / 2;
     if (wave < kNW / 2)
-      gemm_item_rows<NRB, RB0, MB, kNW, 2, S, SWIGLU, F8>(a, lds, wave, lane, 0);
+      gemm_item_rows<NRB, RB0, MB, kNW, 2, S, SWIGLU, F8, NT>(a, lds, wave, lane, 0);
     else
-      gemm_item_rows<NRB, NRB - RB0, MB, kNW, 2, S, SWIGLU, F8>(a, lds, wave, lane, RB0);
+      gemm_item_rows<NRB, NRB - RB0, MB, kNW, 2, S, SWIGLU, F8, NT>(a, lds, wave, lane, RB0);
   }
 }
 
-template <int N, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
+template <int N, int MB, int kNW, int RG, int S, bool SWIGLU, bool F8, bool NT>
 __device__ __forceinline__ void gemm_item_dispatch(int nrb, const ItemArgs& a, uint8_t* lds,
                                                    int wave, int lane) {
   if constexpr (N > MB) {
     return;
   } else {
-    if (nrb == N) gemm_item<N, MB, kNW, RG, S, SWIGLU, F8>(a, lds, wave, lane);
-    else gemm_item_dispatch<N + 1, MB, kNW, RG, S, SWIGLU, F8>(nrb, a, lds, wave, lane);
+    if (nrb == N) gemm_item<N, MB, kNW, RG, S, SWIGLU, F8, NT>(a, lds, wave, lane);
+    else gemm_item_dispatch<N + 1, MB, kNW, RG, S, SWIGLU, F8, NT>(nrb, a, lds, wave, lane);
   }
 }
 
-template <int MB, int kNW, int RG, int S, bool SWIGLU, bool F8>
+template <int MB, int kNW, int RG, int S, bool SWIGLU, bool F8, bool NT>
 __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather, int topk,
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
@@ -590,7 +587,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
                w_expert_stride, plan_expert, q, grid, total, nt_n,
                F8 ? scales + (size_t)e * scale_stride : nullptr};
     const int nrb = (a.nrows + 15) >> 4;
-    gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU, F8>(nrb, a, lds, wave, lane);
+    gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU, F8, NT>(nrb, a, lds, wave, lane);
   }
 }
 
@@ -659,14 +656,14 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
 // S * (16 + MB) KB.  Small m-tiles use 4 waves and fit two workgroups per CU;
 // large ones use 8 waves (two per SIMD) in one workgroup, as 2 row groups x 4
 // column groups.
-template <int MB, int NW, int RG, int S, bool SWIGLU, bool F8 = false>
+template <int MB, int NW, int RG, int S, bool SWIGLU, bool F8 = false, bool NT = (MB <= 8)>
 static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int topk,
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                 int packed, const LoraArgs& lora, int64_t max_items,
                                 hipStream_t stream, const float* scales = nullptr,
                                 int64_t scale_stride = 0) {
-  auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU, F8>;
+  auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU, F8, NT>;
   static int per_cu = 0;  // resident workgroups per CU, fixed per build
   static int cus = 0;
   if (per_cu == 0) {
@@ -711,6 +708,17 @@ int ffn_choose_mb(int64_t rows, int E) {
 
 int ffn_out_cols_per_item(bool swiglu) { return swiglu ? kColsGateUp : kColsDown; }
 
+// Up to 128-row tiles (batches of up to ~2.5K tokens) the kernel is a pure
+// weight stream and always loads weights non-temporally (6.6 TB/s against
+// 6.1 with the default policy at decode).  The 192-row gate/up GEMM does so
+// while the mean expert holds at most 160 rows: nearly every expert is then
+// a single m-tile whose weights are read once (4096-token chunk: 2.41 ->
+// 2.34 ms).  With more rows per expert (the skewed 16K-token batch re-reads
+// hot experts' weights for several m-tiles) the default policy keeps those
+// re-reads in the caches (non-temporal: 7.6 -> 8.4 ms), and the 192-row down
+// GEMM was 2-4 % slower with non-temporal loads in both cases.
+bool ffn_stream_weights(int64_t rows, int E) { return rows / (E > 0 ? E : 1) <= 160; }
+
 hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* plan, int max_tiles,
                             hipStream_t stream) {
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, stream, offsets, E, bmax, plan,
@@ -731,25 +739,32 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                int packed, const LoraArgs& lora, int64_t max_items,
-                               hipStream_t stream) {
-#define BEAM_STREAM_CASE(MBV, NWV, RGV, SV)                                                     \
-  case MBV:                                                                                     \
-    return swiglu ? launch_stream<MBV, NWV, RGV, SV, true>(A, gather, topk, W, wstride, C,      \
-                                                           plan, max_tiles, K, n_out, up_row0,  \
-                                                           packed, lora, max_items, stream)     \
-                  : launch_stream<MBV, NWV, RGV, SV, false>(A, gather, topk, W, wstride, C,     \
-                                                            plan, max_tiles, K, n_out, up_row0, \
-                                                            packed, lora, max_items, stream);
+                               hipStream_t stream, bool stream_weights) {
+#define BEAM_STREAM_ARGS                                                                    \
+  A, gather, topk, W, wstride, C, plan, max_tiles, K, n_out, up_row0, packed, lora, max_items, \
+      stream
+#define BEAM_STREAM_CASE(MBV, NWV, RGV, SV)                                \
+  case MBV:                                                                \
+    return swiglu ? launch_stream<MBV, NWV, RGV, SV, true>(BEAM_STREAM_ARGS) \
+                  : launch_stream<MBV, NWV, RGV, SV, false>(BEAM_STREAM_ARGS);
   switch (mb) {
     BEAM_STREAM_CASE(4, 4, 1, BEAM_GEMM_S4)
     BEAM_STREAM_CASE(8, BEAM_GEMM_NW8, BEAM_GEMM_RG8, BEAM_GEMM_S8)
 #if BEAM_GEMM_MAXMB != 8
-    BEAM_STREAM_CASE(BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12, BEAM_GEMM_S12)
+    case BEAM_GEMM_MAXMB:
+      if (swiglu && stream_weights)
+        return launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12, BEAM_GEMM_S12, true,
+                             false, true>(BEAM_STREAM_ARGS);
+      return swiglu ? launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12,
+                                    BEAM_GEMM_S12, true>(BEAM_STREAM_ARGS)
+                    : launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12,
+                                    BEAM_GEMM_S12, false>(BEAM_STREAM_ARGS);
 #endif
     default:
       return hipErrorInvalidValue;
   }
 #undef BEAM_STREAM_CASE
+#undef BEAM_STREAM_ARGS
 }
 
 // FP8 (E4M3FN) weights through the same 64-k stage pipeline: a weight stage

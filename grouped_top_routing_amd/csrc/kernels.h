@@ -44,7 +44,10 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                int packed, const LoraArgs& lora, int64_t max_items,
-                               hipStream_t stream);
+                               hipStream_t stream, bool stream_weights);
+// whether the gate/up GEMM of a batch of `rows` (token, expert) pairs over E
+// experts loads its weights non-temporally (only the 192-row tiles differ)
+bool ffn_stream_weights(int64_t rows, int E);
 hipError_t launch_lora_a(const uint16_t* X, const int32_t* gather, int topk, const uint16_t* La,
                          int K, int rank, float scale, uint16_t* t, const int32_t* plan,
                          int max_tiles, hipStream_t stream);
