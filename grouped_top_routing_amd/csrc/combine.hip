@@ -1,8 +1,9 @@
 // Weighted un-permute of the Beam-1.0 MoE block on gfx950.
 //
 // "Welcome Beam: a 501B open model you can own, customize, and scale", section
-// "Mixture of Experts": the chosen experts' outputs are combined with the
-// normalized router weights and scaled by 2.5; there is no shared expert.
+// "Mixture of Experts": a token's output sums its chosen experts' outputs,
+// each weighted by its score over the sum of the chosen scores, and multiplies
+// the sum by 2.5; there is no shared expert.
 //
 // out[t, :] = bf16( scale * sum_j w[t, j] * y[perm_dst[t*topk + j], :] ), the
 // sum taken in fp32 in slot order.  Workgroup (t, c) handles token t's c-th

@@ -4,7 +4,7 @@
 // "Mixture of Experts": every expert gets a sigmoid score; the experts form 8
 // groups of 32; the 4 groups with the largest sum of their two best scores are
 // kept; the 8 best experts inside them are chosen; their outputs are later
-// combined with normalized router weights.  The router runs in FP32 (same page,
+// summed with weights proportional to their scores (summing to one).  The router runs in FP32 (same page,
 // section "Residual Stream"; "Beam 1.0" miles recipes, section 1: router weights
 // stay FP32).
 //
@@ -285,7 +285,10 @@ __global__ __launch_bounds__(256) void select_kernel(
   }
 }
 
-// Routing replay: scores of caller-given experts, weights only.
+// Routing replay: scores of caller-given experts, weights only.  An id
+// outside [0, E) is dropped, as the permutation drops it: its weight is 0 and
+// its slot takes no part in the normalising sum (a token whose ids are all
+// dropped gets weights 0).
 __global__ __launch_bounds__(256) void replay_kernel(
     const float* __restrict__ part, int splits, const int32_t* __restrict__ ids,
     float* __restrict__ wout, int T, int E, int topk, int renormalize) {
@@ -294,15 +297,17 @@ __global__ __launch_bounds__(256) void replay_kernel(
   if (t >= T) return;
   float my_s = 0.f;
   if (lane < topk) {
-    int e = ids[(size_t)t * topk + lane];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    float lg = 0.f;
-    for (int s = 0; s < splits; ++s) lg += part[((size_t)s * T + t) * E + e];
-    my_s = sigmoidf_(lg);
+    const int e = ids[(size_t)t * topk + lane];
+    if (e >= 0 && e < E) {
+      float lg = 0.f;
+      for (int s = 0; s < splits; ++s) lg += part[((size_t)s * T + t) * E + e];
+      my_s = sigmoidf_(lg);
+    }
   }
   float ssum = 0.f;
   for (int j = 0; j < topk; ++j) ssum += __shfl(my_s, j);
-  if (lane < topk) wout[(size_t)t * topk + lane] = renormalize ? my_s / ssum : my_s;
+  if (lane < topk)
+    wout[(size_t)t * topk + lane] = renormalize ? (ssum > 0.f ? my_s / ssum : 0.f) : my_s;
 }
 
 // ---------------------------------------------------------------------------

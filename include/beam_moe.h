@@ -13,8 +13,8 @@
  *   4. the topk best experts inside the kept groups are chosen,
  *   5. each chosen expert is a SwiGLU MLP (gate/up projection, SiLU(gate)*up
  *      in FP32, down projection), with no shared expert,
- *   6. expert outputs are combined with the normalized router weights and
- *      scaled by routed_scaling (2.5).
+ *   6. the token's output is the sum of its experts' outputs, each weighted by
+ *      its score over the sum of the chosen scores, times routed_scaling (2.5).
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -79,7 +79,7 @@ typedef struct moe_config {
   int32_t topk_groups;    /* groups kept per token, 4                             */
   int32_t topk;           /* experts per token, 8                                 */
   int32_t renormalize;    /* 1: combine weight = score / sum of the topk chosen
-                             scores ("normalized router weights"); 0: raw score   */
+                             scores (weights that sum to one); 0: raw score       */
   float routed_scaling;   /* factor applied to the combined output, 2.5          */
   int32_t weight_layout;  /* expert weight storage: MOE_LAYOUT_ROW_MAJOR or
                              MOE_LAYOUT_PACKED (written by moe_pack_weights) for
@@ -121,8 +121,13 @@ int moe_route(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
 /*
  * Routing replay: recompute scores and combine weights for caller-supplied
  * expert ids (e.g. recorded at rollout time), skipping selection.
- *   topk_ids  [T, topk] int32 in, each in [0, E)
+ *   topk_ids  [T, topk] int32 in; an id outside [0, E) names no expert and is
+ *             dropped, as moe_permute drops it: its weight is 0 and it is left
+ *             out of the normalising sum (a token with no valid id gets all
+ *             weights 0)
  *   topk_w    [T, topk] fp32 out
+ * Replayed ids then go through moe_permute, the expert calls and moe_combine,
+ * where a dropped slot contributes nothing.
  */
 int moe_route_replay(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
                      const int32_t* topk_ids, float* topk_w,

@@ -11,7 +11,8 @@ Sources (page titles and sections):
   section "Mixture of Experts": 256 SwiGLU experts of intermediate size 2,560;
   sigmoid scores over all 256 experts; 8 groups of 32; keep the 4 groups with
   the largest sum of their two best scores; top 8 experts inside them; no shared
-  expert; outputs combined with normalized router weights and scaled by 2.5.
+  expert; each token's output is the sum of its chosen experts' outputs, each
+  weighted by its score divided by the sum of the chosen scores, times 2.5.
   Same page, section "Residual Stream": the router and the SwiGLU product are
   computed in FP32.
 * "Beam 1.0" (miles launch recipes), section 1 "Model Introduction": grouped
@@ -139,11 +140,21 @@ def route(x, w_router, *, n_groups=8, topk_groups=4, topk=8, renormalize=True, s
 
 def route_replay(x, w_router, ids, *, renormalize=True):
     """Routing replay: caller-supplied expert ids; only the router GEMM, the
-    sigmoid and the combine weights are recomputed."""
+    sigmoid and the combine weights are recomputed.  An id outside [0, E)
+    names no expert and is dropped (the reading matches ``permute``): its
+    weight is 0 and it is left out of the normalising sum; a token with no
+    valid id gets weights 0."""
     logits = router_logits(x, w_router)
     scores = sigmoid_f32(logits)
     ids = np.asarray(ids, dtype=np.int64)
-    return _weights(scores, ids, renormalize), scores
+    E = scores.shape[1]
+    valid = (ids >= 0) & (ids < E)
+    r = np.where(valid, np.take_along_axis(scores.astype(np.float64), np.clip(ids, 0, E - 1),
+                                           axis=1), 0.0)
+    if renormalize:
+        tot = r.sum(axis=1, keepdims=True)
+        r = np.divide(r, tot, out=np.zeros_like(r), where=tot > 0)
+    return r, scores
 
 
 def permute(ids, n_experts):
@@ -151,14 +162,18 @@ def permute(ids, n_experts):
 
     Row r of the permuted order holds flat slot perm_src[r] = t*k + j; rows are
     ordered by expert, then by token (slot index) ascending.  perm_dst is the
-    inverse: perm_dst[t*k + j] = r.
+    inverse: perm_dst[t*k + j] = r.  A slot whose id lies outside
+    [0, n_experts) names no expert: it is not counted, has no row
+    (perm_dst = -1), and perm_src holds only the offsets[-1] valid rows.
     """
     flat = np.asarray(ids, dtype=np.int64).reshape(-1)
-    counts = np.bincount(flat, minlength=n_experts).astype(np.int64)
+    valid = (flat >= 0) & (flat < n_experts)
+    counts = np.bincount(flat[valid], minlength=n_experts).astype(np.int64)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
-    perm_src = np.argsort(flat, kind="stable").astype(np.int64)
-    perm_dst = np.empty_like(perm_src)
-    perm_dst[perm_src] = np.arange(flat.size)
+    slots = np.nonzero(valid)[0]
+    perm_src = slots[np.argsort(flat[slots], kind="stable")].astype(np.int64)
+    perm_dst = np.full(flat.size, -1, dtype=np.int64)
+    perm_dst[perm_src] = np.arange(perm_src.size)
     return counts, offsets, perm_src, perm_dst
 
 
@@ -237,9 +252,14 @@ def expert_ffn(x, perm_src, offsets, experts, topk=8, lora=None, lora_scale_=Non
 
 
 def combine(y_perm, perm_dst, weights, scale=2.5):
-    """out[t] = scale * sum_j w[t, j] * y_perm[perm_dst[t*k + j]], in fp64."""
+    """out[t] = scale * sum_j w[t, j] * y_perm[perm_dst[t*k + j]], in fp64;
+    slots without a row (perm_dst < 0) contribute nothing."""
     T, k = weights.shape
-    rows = np.asarray(y_perm, dtype=np.float64)[np.asarray(perm_dst).reshape(T, k)]
+    dst = np.asarray(perm_dst).reshape(T, k)
+    y = np.asarray(y_perm, dtype=np.float64)
+    rows = np.zeros((T, k, y.shape[1]))
+    has = dst >= 0
+    rows[has] = y[dst[has]]
     return scale * np.einsum("tj,tjh->th", np.asarray(weights, dtype=np.float64), rows)
 
 

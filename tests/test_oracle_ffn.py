@@ -2,8 +2,9 @@
 
 What is pinned ("Welcome Beam: a 501B open model you can own, customize, and
 scale", section Mixture of Experts): each expert is a SwiGLU MLP; outputs of
-the 8 chosen experts are combined with normalized router weights and scaled by
-2.5; there is no shared expert.  Checks use a library SwiGLU (torch, fp64, CPU),
+the 8 chosen experts are summed with weights equal to each score over the sum
+of the chosen scores, and the sum is multiplied by 2.5; there is no shared
+expert.  Checks use a library SwiGLU (torch, fp64, CPU),
 closed forms with identical or proportional experts, and invariants.
 """
 import numpy as np
@@ -162,3 +163,66 @@ def test_combine_weighted_sum_by_hand(renorm):
     out = oracle.combine(y, perm_dst, w, 2.5)
     np.testing.assert_allclose(out[0], 2.5 * (0.25 * y[2] + 0.75 * y[0]))
     np.testing.assert_allclose(out[1], 2.5 * (0.5 * y[3] + 0.5 * y[1]))
+
+
+def _bad_ids(rng, T, E=256):
+    ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(T)]).astype(np.int64)
+    ids[1, 3] = -1            # one dropped slot
+    ids[4, 0] = E             # one past the last expert
+    ids[6, :] = -7            # a token with no valid id
+    ids[9, 7] = 1 << 30
+    return ids
+
+
+def test_permute_drops_invalid_ids_by_loop():
+    # brute force: for every expert in turn, the slots naming it in increasing
+    # order; slots naming no expert get no row
+    rng = np.random.default_rng(41)
+    ids = _bad_ids(rng, 40)
+    counts, offsets, perm_src, perm_dst = oracle.permute(ids, 256)
+    flat = ids.reshape(-1)
+    want = [s for e in range(256) for s in range(flat.size) if flat[s] == e]
+    assert list(perm_src) == want
+    assert counts.sum() == len(want) == offsets[-1] == 8 * 40 - 11
+    for s in range(flat.size):
+        if 0 <= flat[s] < 256:
+            assert perm_src[perm_dst[s]] == s
+        else:
+            assert perm_dst[s] == -1
+
+
+def test_replay_drops_invalid_ids():
+    # a dropped slot has weight 0, and the other slots' weights are those of a
+    # replay of the valid ids alone (normalised over them)
+    rng = np.random.default_rng(42)
+    x, wr, gu, dn = _rand_layer(rng, T=12)
+    ids = _bad_ids(rng, 12)
+    for renorm in (True, False):
+        w, s = oracle.route_replay(x, wr, ids, renormalize=renorm)
+        for t in range(12):
+            ok = (ids[t] >= 0) & (ids[t] < 256)
+            assert np.all(w[t, ~ok] == 0)
+            if ok.any():
+                wv, _ = oracle.route_replay(x[t:t + 1], wr, ids[t:t + 1, ok], renormalize=renorm)
+                np.testing.assert_allclose(w[t, ok], wv[0], rtol=1e-14)
+                r = s[t, ids[t, ok]].astype(np.float64)
+                np.testing.assert_allclose(w[t, ok], r / r.sum() if renorm else r, rtol=1e-14)
+
+
+def test_layer_with_dropped_ids_by_hand():
+    # the replayed layer with dropped slots: each token's output is 2.5 times
+    # the weighted sum over its valid slots only, worked token by token
+    rng = np.random.default_rng(43)
+    x, wr, gu, dn = _rand_layer(rng, T=12)
+    ids = _bad_ids(rng, 12)
+    res = oracle.layer_forward(x, wr, (gu, dn), ids=ids)
+    s = oracle.sigmoid_f32(oracle.router_logits(x, wr)).astype(np.float64)
+    for t in range(12):
+        ok = [j for j in range(8) if 0 <= ids[t, j] < 256]
+        want = np.zeros(x.shape[1])
+        tot = sum(s[t, ids[t, j]] for j in ok)
+        for j in ok:
+            e = ids[t, j]
+            want += s[t, e] / tot * oracle.ffn_rows(x[t:t + 1], gu[e], dn[e])[0]
+        np.testing.assert_allclose(res["out"][t], 2.5 * want, rtol=1e-10, atol=1e-12)
+    assert np.all(res["out"][6] == 0)

@@ -48,6 +48,43 @@ def test_hand_cases_through_router(golden_dir):
         assert list(rr.ids[0]) == case["ids"], case["name"]
         if "weights" in case:
             np.testing.assert_allclose(rr.weights[0], case["weights"], rtol=1e-6)
+        if "weights_unnormalised" in case:
+            raw = oracle.route(np.ones((1, 1), np.float32), w, renormalize=False)
+            np.testing.assert_allclose(raw.weights[0], case["weights_unnormalised"], rtol=1e-6)
+
+
+def test_normalised_weights_by_hand(golden_dir):
+    # unequal chosen scores: the normalised weights are each score over the sum
+    # of the eight chosen scores (hand-worked in the fixture), which neither a
+    # softmax over the chosen scores nor a division by the sum of all 256
+    # scores reproduces
+    case = {c["name"]: c for c in _load_cases(golden_dir)}["unequal_scores_normalised"]
+    s = _scores_from_case(case)
+    ids = np.array([case["ids"]], dtype=np.int64)
+    w = oracle._weights(s[None, :], ids, True)
+    np.testing.assert_allclose(w[0], case["weights"], rtol=1e-6)
+    np.testing.assert_allclose(oracle._weights(s[None, :], ids, False)[0],
+                               case["weights_unnormalised"], rtol=1e-6)
+    soft = np.exp(np.float64(case["weights_unnormalised"]))
+    assert not np.allclose(case["weights"], soft / soft.sum(), rtol=1e-3)
+    assert not np.allclose(case["weights"], s[case["ids"]] / s.sum(dtype=np.float64), rtol=1e-3)
+
+
+def test_normalised_and_raw_weights_relation():
+    # with normalisation on, the weights are the raw (normalisation off)
+    # weights divided by their per-token sum; the raw weights are the chosen
+    # experts' own sigmoid scores, so their ratios are the score ratios
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((64, 96)).astype(np.float32)
+    w = (0.3 * rng.standard_normal((256, 96))).astype(np.float32)
+    on = oracle.route(x, w, renormalize=True)
+    off = oracle.route(x, w, renormalize=False)
+    assert np.array_equal(on.ids, off.ids)
+    raw = off.weights
+    assert np.ptp(raw, axis=1).min() > 1e-4          # the chosen scores are unequal
+    np.testing.assert_allclose(on.weights, raw / raw.sum(axis=1, keepdims=True), rtol=1e-12)
+    np.testing.assert_allclose(on.weights[:, 0] / on.weights[:, 1], raw[:, 0] / raw[:, 1],
+                               rtol=1e-12)
 
 
 def _brute_force(sel_row, G, KG, K):
