@@ -342,10 +342,13 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     };
 
     // Prologue.  Every item except a workgroup's first finds its first kPre
-    // weight stages issued by its predecessor.
+    // weight stages issued by its predecessor.  Stages at or past nst do not
+    // exist (K = 128 has two) and are never issued; leaving out such older
+    // loads only lowers the counts the waits below have to reach.
     if (a.q < a.grid) {
 #pragma unroll
-      for (int P = 0; P < kPre; ++P) issue_b64(bsrc, P);
+      for (int P = 0; P < kPre; ++P)
+        if (P < nst) issue_b64(bsrc, P);
     }
 #pragma unroll
     for (int P = kPre; P < S - 1; ++P)
@@ -486,8 +489,10 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       const uint8_t* nsrc[NBL];
 #pragma unroll
       for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
+      const int nst = a.K / (2 * kBKS);  // the next item's k stages (same K)
 #pragma unroll
-      for (int P = 0; P < kPre; ++P) issue_b64(nsrc, P);
+      for (int P = 0; P < kPre; ++P)
+        if (P < nst) issue_b64(nsrc, P);
     }
   }
 

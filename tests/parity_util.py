@@ -33,6 +33,7 @@ def assert_close(y, r, what, max_rel=MAX_REL, mean_rel=MEAN_REL):
     say(f"  {what}: max_rel={mx:.3e} mean_rel={mn:.3e} rms={rms:.3e}")
     assert mx <= max_rel, f"{what}: max relative error {mx:.3e} > {max_rel}"
     assert mn <= mean_rel, f"{what}: mean abs error {mn:.3e} > {mean_rel} * RMS"
+    return mx, mn
 
 
 def to_np(t):

@@ -87,18 +87,6 @@ def test_route_200_tokens():
 
 
 # ------------------------------------------------------------------- permute
-def _expected_perm(ids, E=256):
-    flat = ids.reshape(-1).astype(np.int64)
-    valid = (flat >= 0) & (flat < E)
-    counts = np.bincount(flat[valid], minlength=E)
-    offsets = np.concatenate([[0], np.cumsum(counts)])
-    idx = np.nonzero(valid)[0]
-    order = idx[np.argsort(flat[idx], kind="stable")]
-    dst = np.full(flat.size, -1, np.int64)
-    dst[order] = np.arange(order.size)
-    return counts, offsets, order, dst
-
-
 @pytest.mark.parametrize("T,hot", [(1, None), (3, None), (128, None), (513, None), (4097, None),
                                    (2000, list(range(100, 108)))])
 def test_permute_exact(T, hot):
@@ -119,11 +107,56 @@ def test_permute_drops_out_of_range_ids():
     ids[77, 0] = 256
     ids[299, 7] = 1 << 30
     c, o, ps, pd = gtr.permute(torch.from_numpy(ids).to(DEV))
-    rc, ro, rorder, rdst = _expected_perm(ids)
+    rc, ro, rorder, rdst = oracle.permute(ids, 256)
     n = int(ro[-1])
+    assert n == 300 * 8 - 3
     assert np.array_equal(to_np(c), rc) and np.array_equal(to_np(o), ro)
     assert np.array_equal(to_np(ps)[:n], rorder)
     assert np.array_equal(to_np(pd), rdst)
+
+
+def _with_bad_ids(ids):
+    ids = ids.copy()
+    ids[1, 3] = -1
+    ids[4, 0] = 256
+    ids[6, :] = -7          # a token with no valid id
+    ids[9, 7] = 1 << 30
+    return ids
+
+
+def test_route_replay_drops_out_of_range_ids(tiny):
+    # ids outside [0, E) get weight 0 and leave the normalising sum, as the
+    # permutation drops them
+    say("[route_replay] out-of-range ids")
+    rr = oracle.route(tiny["np"]["x"], tiny["np"]["w_router"])
+    bad = _with_bad_ids(rr.ids.astype(np.int32))
+    ids = torch.from_numpy(bad).to(DEV)
+    for renorm in (True, False):
+        w = gtr.route_replay(tiny["x"], tiny["w_router"], ids, renormalize=renorm)
+        ref, _ = oracle.route_replay(tiny["np"]["x"], tiny["np"]["w_router"], bad,
+                                     renormalize=renorm)
+        got = to_np(w)
+        assert np.all(got[(bad < 0) | (bad >= 256)] == 0) and np.all(got[6] == 0)
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-7)
+
+
+def test_replayed_layer_with_dropped_ids(tiny):
+    # the staged block on replayed ids with dropped slots against the oracle's
+    # layer on the same ids
+    say("[layer] replayed ids with out-of-range entries")
+    npd = tiny["np"]
+    rr = oracle.route(npd["x"], npd["w_router"])
+    bad = _with_bad_ids(rr.ids.astype(np.int32))
+    ids = torch.from_numpy(bad).to(DEV)
+    w = gtr.route_replay(tiny["x"], tiny["w_router"], ids)
+    c, o, ps, pd = gtr.permute(ids)
+    y = gtr.expert_ffn(tiny["x"], ps, o, tiny["w_gate_up"], tiny["w_down"])
+    out = gtr.combine(y, pd, w)
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(npd["x"], npd["w_router"], (npd["w_gate_up"], npd["w_down"]),
+                               ids=bad)
+    assert np.all(to_np(out)[6] == 0)
+    assert_close(to_np(out), ref["out"], "out with dropped slots")
 
 
 # ----------------------------------------------------------------------- ffn
