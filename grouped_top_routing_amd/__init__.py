@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     ENTRY_PERMUTE, ENTRY_ROUTE, EXPORTS, LoraWeights, MoeLora, expert_ffn_lora, layer_forward_lora,
     LAYOUT_FP8_PACKED, LAYOUT_PACKED, LAYOUT_ROW_MAJOR, LIB_PATH, Fp8Weights, MoeConfig,
     MoeError, Workspace, combine, expert_down, expert_down_fp8, expert_ffn, expert_ffn_fp8,
-    expert_gate_up, expert_gate_up_fp8, layer_forward, layer_forward_fp8, lib, make_config,
+    expert_gate_up, expert_gate_up_fp8, layer_forward, layer_forward_fp8,
+    layer_forward_noalloc, lib, make_config,
     pack_weights, permute, quantize_fp8, route, route_replay, status_string, workspace_bytes,
 )

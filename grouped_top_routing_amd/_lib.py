@@ -20,6 +20,7 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_TOO_LARGE = -5
 
 ENTRY_ROUTE = 0
 ENTRY_PERMUTE = 1
@@ -38,7 +39,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_replay", "moe_permute"
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
            "moe_layer_forward", "moe_pack_weights", "moe_quantize_fp8", "moe_expert_ffn_fp8",
            "moe_expert_gate_up_fp8", "moe_expert_down_fp8", "moe_layer_forward_fp8",
-           "moe_expert_ffn_lora", "moe_layer_forward_lora", "moe_status_string")
+           "moe_expert_ffn_lora", "moe_layer_forward_lora", "moe_layer_forward_noalloc",
+           "moe_status_string")
 
 
 class MoeConfig(ctypes.Structure):
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [CP, P, P, P, P, P]
         L.moe_pack_weights.argtypes = [CP, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
+        L.moe_layer_forward_noalloc.argtypes = [CP, P, P, P, P, P, P, P, P, P]
         L.moe_quantize_fp8.argtypes = [CP, P, P, P, P, P, P, P]
         L.moe_expert_ffn_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
         L.moe_expert_gate_up_fp8.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
@@ -349,6 +352,40 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, sel_bias=None, num_groups=8
                                   _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(ids), _ptr(w),
                                   _ptr(ws), nb, _stream(x.device)))
     return (out, ids, w) if return_routing else out
+
+
+def layer_forward_noalloc(x, w_router, w_gate_up, w_down, *, sel_bias=None, num_groups=8,
+                          topk_groups=4, topk=8, renormalize=True, routed_scaling=2.5,
+                          weight_layout=LAYOUT_ROW_MAJOR, out=None, ids=None, w=None):
+    """moe_layer_forward_noalloc: the whole block with the library's static
+    scratch array instead of a workspace.  ``out`` (bf16 [T, H]) and the
+    optional routing outputs ``ids`` (int32 [T, k]) and ``w`` (fp32 [T, k])
+    may be passed preallocated; the library call itself allocates nothing.
+    Returns out, or (out, ids, w) when ids or w are given."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    _check(x, "x", torch.bfloat16)
+    _check(w_router, "w_router", torch.float32, (E, H), x.device)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * I, H), x.device)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), x.device)
+    if sel_bias is not None:
+        _check(sel_bias, "sel_bias", torch.float32, (E,), x.device)
+    for t, name, dt in ((ids, "ids", torch.int32), (w, "w", torch.float32)):
+        if t is not None:
+            _check(t, name, dt, (T, topk), x.device)
+    cfg = make_config(T, H, I, num_experts=E, num_groups=num_groups, topk_groups=topk_groups,
+                      topk=topk, renormalize=renormalize, routed_scaling=routed_scaling,
+                      weight_layout=weight_layout)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    else:
+        _check(out, "out", torch.bfloat16, (T, H), x.device)
+    _call("moe_layer_forward_noalloc",
+          lib().moe_layer_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_router),
+                                          _ptr(sel_bias), _ptr(w_gate_up), _ptr(w_down),
+                                          _ptr(out), _ptr(ids), _ptr(w), _stream(x.device)))
+    return out if ids is None and w is None else (out, ids, w)
 
 
 def pack_weights(w_gate_up=None, w_down=None):

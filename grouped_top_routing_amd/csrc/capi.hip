@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/beam_moe.h"
 #include "kernels.h"
@@ -295,6 +296,40 @@ bool layer_args_ok(const moe_config_t* cfg, const uint16_t* x, const float* w_ro
          (!topk_w_out || aligned4(topk_w_out));
 }
 
+// ---- scratch for moe_layer_forward_noalloc ----
+// The one scratch buffer of the library that no caller provides: a static
+// device array, one copy per GPU the library runs on, held until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol); it reads the device address once per
+// device with hipGetSymbolAddress and passes that on.
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device (with it current) and kept.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,6 +341,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by the gfx950 kernels";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    case MOE_ERR_TOO_LARGE:
+      return "MOE_ERR_TOO_LARGE: the call needs more scratch than the library's static 128 MiB";
     default: return "unknown moe status";
   }
 }
@@ -491,6 +528,27 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
                       workspace_bytes, s,
                       [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* scratch) {
                         return do_ffn(cfg, x, psrc, offsets, w_gate_up, w_down, y, scratch, s);
+                      });
+}
+
+int moe_layer_forward_noalloc(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                              const float* sel_bias, const uint16_t* w_gate_up,
+                              const uint16_t* w_down, uint16_t* out, int32_t* topk_ids_out,
+                              float* topk_w_out, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (!layer_args_ok(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out) || !w_gate_up ||
+      !w_down || !aligned16(w_gate_up) || !aligned16(w_down))
+    return MOE_ERR_INVALID_ARG;
+  if (layer_layout(cfg).total > kNoAllocScratchBytes) return MOE_ERR_TOO_LARGE;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return layer_common(cfg, x, w_router, sel_bias, out, topk_ids_out, topk_w_out, ws,
+                      kNoAllocScratchBytes, s,
+                      [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* sc) {
+                        return do_ffn(cfg, x, psrc, offsets, w_gate_up, w_down, y, sc, s);
                       });
 }
 

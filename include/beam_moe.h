@@ -56,7 +56,9 @@ enum moe_status {
   MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative size, misalignment     */
   MOE_ERR_UNSUPPORTED = -2,  /* valid but outside the shapes listed above     */
   MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required    */
-  MOE_ERR_HIP = -4           /* HIP runtime error (no device, launch failure) */
+  MOE_ERR_HIP = -4,          /* HIP runtime error (no device, launch failure) */
+  MOE_ERR_TOO_LARGE = -5     /* moe_layer_forward_noalloc: the call needs more
+                                scratch than the library's static array holds */
 };
 
 /* Which entry point a workspace size is asked for. */
@@ -197,6 +199,27 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
                       const float* sel_bias, const uint16_t* w_gate_up, const uint16_t* w_down,
                       uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with no workspace argument.  The
+ * scratch comes from a static device array of 128 MiB inside the library, one
+ * per GPU it runs on, held until the process ends; the call allocates nothing.
+ *   - It serves configurations whose moe_workspace_bytes(MOE_ENTRY_LAYER) is at
+ *     most 128 MiB (at the Beam shape, hidden 5120 and intermediate 2560:
+ *     batches of up to 512 tokens); larger ones return MOE_ERR_TOO_LARGE and
+ *     enqueue nothing.
+ *   - It uses the array of the current device; `stream` must belong to it.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind: calls that overlap on one GPU (on different streams, or from
+ *     several threads without ordering) race.  Order them on one stream.
+ * Other arguments are those of moe_layer_forward.
+ */
+int moe_layer_forward_noalloc(const moe_config_t* cfg, const uint16_t* x, const float* w_router,
+                              const float* sel_bias, const uint16_t* w_gate_up,
+                              const uint16_t* w_down, uint16_t* out, int32_t* topk_ids_out,
+                              float* topk_w_out, void* stream);
 
 /*
  * Rewrites expert weights from MOE_LAYOUT_ROW_MAJOR into MOE_LAYOUT_PACKED

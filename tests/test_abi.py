@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert gtr.status_string(code).startswith("MOE_")
     assert "unknown" in gtr.status_string(7)
 
