@@ -50,6 +50,10 @@ def parse():
                    help="experts whose rows the CPU oracle processes in its timed sample")
     p.add_argument("--no-row-major-ref", action="store_true",
                    help="skip the reference timing with row-major weights (profiling runs)")
+    p.add_argument("--no-parity", action="store_true",
+                   help="skip the oracle comparison of the decode, mid and skewed outputs")
+    p.add_argument("--decode-seeds", type=int, default=4,
+                   help="seeds of the decode batch to time (the touched-expert count varies)")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="run one device-to-device copy of this size first (a known byte "
                         "count for scaling hardware byte counters)")
@@ -57,30 +61,46 @@ def parse():
 
 
 def git_sha():
+    """The commit the library was built from (recorded by the build next to
+    the library; a snapshot without .git has no other source), and whether the
+    tree had uncommitted changes then."""
+    info = {}
     try:
-        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
-                              text=True, timeout=10).stdout.strip() or None
-    except Exception:
-        return None
+        with open(os.path.join(ROOT, "grouped_top_routing_amd", "_build_info.json")) as f:
+            info = json.load(f)
+    except (OSError, ValueError):
+        pass
+    if not info.get("git"):
+        try:
+            sha = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT,
+                                 capture_output=True, text=True, timeout=10).stdout.strip()
+            info = {"git": sha or None, "source": "git at run time"}
+        except Exception:
+            pass
+    return info or None
 
 
-PROFILE = os.path.join(ROOT, "profiles", "gate_up_grouped_gemm_prefill_T4096.md")
+PROFILE = os.path.join(ROOT, "profiles", "grouped_gemm_prefill_T4096.md")
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading for
-    a 1 GiB copy), or None when the kernel source changed since they were
-    taken or the summary is missing."""
+def kernel_source_sha256():
     import hashlib
+    return hashlib.sha256(b"".join(
+        open(os.path.join(ROOT, "grouped_top_routing_amd", "csrc", f), "rb").read()
+        for f in ("ffn.hip", "common.h"))).hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` ("gate_up" or "down") from the
+    committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled
+    by the same counter's reading for a 1 GiB copy), or None when the kernel
+    source changed since they were taken or the summary is missing."""
     try:
         text = open(PROFILE).read()
         blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-        src = b"".join(open(os.path.join(ROOT, "grouped_top_routing_amd", "csrc", f), "rb").read()
-                       for f in ("ffn.hip", "common.h"))
-        if hashlib.sha256(src).hexdigest() != blob["kernel_source_sha256"]:
+        if kernel_source_sha256() != blob["kernel_source_sha256"]:
             return None
-        return int(blob["gate_up"]["read_bytes"] + blob["gate_up"]["write_bytes"])
+        return int(blob[kernel]["read_bytes"] + blob[kernel]["write_bytes"])
     except (OSError, IndexError, KeyError, ValueError):
         return None
 
@@ -97,20 +117,26 @@ def algorithmic(w, counts, fmt="bf16"):
     else:
         b_expert = 3 * H * I * 2                  # gate, up, down rows of one expert, bf16
         b_gu = 2 * I * H * 2
+    b_dn = b_expert - b_gu
     layer_bytes = touched * b_expert + w.E * H * 4 + T * H * 2 + T * H * 2
-    gu_bytes = touched * b_gu + T * H * 2 + K * T * I * 2
+    # per kernel: the weights it streams (+ the x rows the gate/up kernel
+    # gathers); the intermediates h and y_perm are implementation traffic
+    gu_bytes = touched * b_gu + T * H * 2
+    dn_bytes = touched * b_dn
     flops = K * T * 2 * 3 * H * I
     return {"touched": touched, "layer_bytes": layer_bytes, "gate_up_bytes": gu_bytes,
-            "expert_flops": flops, "gate_up_flops": K * T * 2 * 2 * H * I}
+            "down_bytes": dn_bytes, "expert_flops": flops,
+            "gate_up_flops": K * T * 2 * 2 * H * I, "down_flops": K * T * 2 * H * I}
 
 
-def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", rowmajor=True):
+def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", rowmajor=True,
+                 seed=None, layer_ref=True):
     """Times `steps` staged layer passes; returns timing dict and routing.
     fmt "bf16": fragment-packed bf16 expert weights; "fp8": E4M3FN codes
     with per-row scales."""
     dev = wts["dev"]
     w = synth.workload(name)
-    x = synth.make_x(w, args.seed, dev, w_router=wts["w_router"])
+    x = synth.make_x(w, args.seed if seed is None else seed, dev, w_router=wts["w_router"])
     wr, wgu, wd = wts["w_router"], wts["p_gate_up"], wts["p_down"]
     lay = gtr.LAYOUT_PACKED
     ws = gtr.Workspace()
@@ -141,7 +167,7 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
         out = gtr.combine(y, pd, tw)
         if ev is not None:
             ev[5].record()
-        return out, ids, c
+        return out, ids, c, tw
 
     for _ in range(warmup):
         step()
@@ -150,7 +176,7 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        out, ids, counts = step(evs[i])
+        out, ids, counts, topw = step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     names = ["route", "permute", "gate_up", "down", "combine"]
@@ -169,7 +195,9 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
             gtr.layer_forward(x, wr, a, b, weight_layout=layout, workspace=ws)
         torch.cuda.synchronize()
         return (time.perf_counter() - t1) * 1e3 / steps
-    if fmt == "fp8":
+    if not layer_ref:
+        layer_ms, rowmajor_ms = None, None
+    elif fmt == "fp8":
         for _ in range(2):
             gtr.layer_forward_fp8(x, wr, f8, workspace=ws)
         torch.cuda.synchronize()
@@ -185,7 +213,61 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
     return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
             "device_step_ms": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
             "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
-            "counts": counts.cpu().numpy(), "ids": ids, "out": out}
+            "counts": counts.cpu().numpy(), "ids": ids, "out": out, "topw": topw}
+
+
+def expert_host(wts, e):
+    """Expert e's bf16 weights on the host as fp64 (exact), moving 2 bytes per
+    element: (gate_up [2I, H], down [H, I])."""
+    import numpy as np
+
+    def conv(t):
+        import torch
+        u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32)
+        return (u << 16).view(np.float32).astype(np.float64)
+    return conv(wts["w_gate_up"][e]), conv(wts["w_down"][e])
+
+
+def north_star_stats(y, r):
+    """max |y - r| / max(|r|, RMS(r)) and mean |y - r| / RMS(r) (the layer
+    output tolerance: 2e-2 and 5e-3)."""
+    import numpy as np
+    rms = float(np.sqrt(np.mean(r * r)))
+    d = np.abs(y - r)
+    return float(np.max(d / np.maximum(np.abs(r), rms))), float(np.mean(d) / rms)
+
+
+def layer_parity(wl, x, out, ids, wts, sample=None, seed=0):
+    """The timed GPU layer output against the oracle on the same input:
+    routing of every token (expert sets; tokens inside the oracle's 1e-5
+    selection margin may differ), then the output over every token, or over
+    `sample` tokens drawn with `seed`, evaluated by the oracle expert by
+    expert on the GPU's expert sets (identical to the oracle's outside the
+    margin) with the oracle's own scores."""
+    import numpy as np
+    import oracle
+    xn = x.float().cpu().numpy()
+    rr = oracle.route(xn, wts["w_router"].cpu().numpy())
+    gid = ids.cpu().numpy().astype(np.int64)
+    same = np.all(np.sort(gid, 1) == np.sort(rr.ids, 1), axis=1)
+    flagged = rr.margin < oracle.MARGIN_TOL
+    T = xn.shape[0]
+    toks = (np.arange(T) if sample is None or sample >= T else
+            np.sort(np.random.default_rng(seed).choice(T, sample, replace=False)))
+    s = rr.scores[toks][np.arange(len(toks))[:, None], gid[toks]].astype(np.float64)
+    wgt = s / s.sum(axis=1, keepdims=True)
+    ref = np.zeros((len(toks), xn.shape[1]))
+    for e in np.unique(gid[toks]):
+        rows, slots = np.nonzero(gid[toks] == e)
+        gu, dn = expert_host(wts, int(e))
+        ref[rows] += wgt[rows, slots][:, None] * oracle.ffn_rows(xn[toks[rows]], gu, dn)
+    ref *= 2.5
+    mx, mn = north_star_stats(out.float().cpu().numpy()[toks].astype(np.float64), ref)
+    return {"tokens": int(T), "output_tokens_compared": int(len(toks)),
+            "routing_sets_differing": int((~same).sum()),
+            "differing_outside_margin": int((~same & ~flagged).sum()),
+            "margin_flagged": int(flagged.sum()), "max_rel": mx, "mean_rel": mn,
+            "within_tolerance": bool(mx <= 2e-2 and mn <= 5e-3 and not (~same & ~flagged).any())}
 
 
 def cpu_baseline(w, x, wts, n_experts, torch, gpu_out=None, gpu_ids=None):
@@ -218,8 +300,7 @@ def cpu_baseline(w, x, wts, n_experts, torch, gpu_out=None, gpu_ids=None):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
             continue
-        gu = wts["w_gate_up"][e].float().cpu().numpy()
-        dn = wts["w_down"][e].float().cpu().numpy()
+        gu, dn = expert_host(wts, e)
         t1 = time.perf_counter()
         y[r0:r1] = oracle.ffn_rows(xn[psrc[r0:r1] // w.K], gu, dn)
         t_ffn += time.perf_counter() - t1
@@ -236,29 +317,60 @@ def cpu_baseline(w, x, wts, n_experts, torch, gpu_out=None, gpu_ids=None):
                       + f": route+permute {t_route:.2f} s, expert MLPs {t_ffn:.2f} s, combine "
                         f"{t_comb:.2f} s; fp64 NumPy/BLAS; host os.cpu_count()={os.cpu_count()}",
             "sample_seconds": round(t_route + t_ffn + t_comb, 2), "blas": blas,
-            "parity": _parity(ref, rr, gpu_out, gpu_ids, rows == w.K * w.T, oracle)}
+            "parity": _parity(ref, rr, gpu_out, gpu_ids, rows == w.K * w.T, xn, wts)}
 
 
-def _parity(ref, rr, gpu_out, gpu_ids, whole, oracle):
-    """The timed GPU output against the oracle's, for the same input: routing
-    sets (tokens within the oracle's selection margin may legitimately
-    differ), and row-wise relative L2 error of the layer output over the
-    tokens routed alike."""
+def _parity(ref, rr, gpu_out, gpu_ids, whole, xn, wts):
+    """The timed GPU output against this oracle run, for the same input:
+    routing sets (tokens within the oracle's selection margin may
+    legitimately differ; such a token's reference is the oracle evaluated on
+    the GPU's set) and the layer-output statistics max |y - r| / max(|r|, RMS)
+    and mean |y - r| / RMS over every token."""
     import numpy as np
+    import oracle
     if gpu_out is None or gpu_ids is None or not whole:
         return None
-    ids = np.sort(gpu_ids.cpu().numpy().astype(np.int64), axis=1)
-    same = np.all(ids == np.sort(rr.ids, axis=1), axis=1)
+    gid = gpu_ids.cpu().numpy().astype(np.int64)
+    same = np.all(np.sort(gid, 1) == np.sort(rr.ids, 1), axis=1)
     flagged = rr.margin < oracle.MARGIN_TOL
-    out = gpu_out.float().cpu().numpy().astype(np.float64)
-    num = np.linalg.norm(out - ref, axis=1)
-    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
-    rel = (num / den)[same]
-    return {"tokens": int(ids.shape[0]), "routing_sets_differing": int((~same).sum()),
+    ref = np.array(ref, copy=True)
+    for t in np.nonzero(~same)[0]:
+        S = gid[t]
+        sc = rr.scores[t, S].astype(np.float64)
+        acc = np.zeros(ref.shape[1])
+        for j, e in enumerate(S):
+            gu, dn = expert_host(wts, int(e))
+            acc += sc[j] / sc.sum() * oracle.ffn_rows(xn[t:t + 1], gu, dn)[0]
+        ref[t] = 2.5 * acc
+    mx, mn = north_star_stats(gpu_out.float().cpu().numpy().astype(np.float64), ref)
+    return {"tokens": int(gid.shape[0]), "output_tokens_compared": int(gid.shape[0]),
+            "routing_sets_differing": int((~same).sum()),
             "differing_outside_margin": int((~same & ~flagged).sum()),
-            "margin_flagged": int(flagged.sum()),
-            "out_rel_l2_max": float(rel.max()) if rel.size else None,
-            "out_rel_l2_mean": float(rel.mean()) if rel.size else None}
+            "margin_flagged": int(flagged.sum()), "max_rel": mx, "mean_rel": mn,
+            "within_tolerance": bool(mx <= 2e-2 and mn <= 5e-3 and not (~same & ~flagged).any())}
+
+
+def kernel_roofline(kernel, alg, stage_ms, workload):
+    """Roofline of one grouped-GEMM launch: algorithmic bytes (the weights of
+    the touched experts it streams, plus the gathered x rows for gate/up) over
+    its average launch time from HIP events on the stream it runs on.  Bound
+    by HBM while the FLOPs per byte stay under the ridge (~315), else by the
+    bf16 matrix cores."""
+    ms = stage_ms[kernel]
+    nbytes, flops = alg[f"{kernel}_bytes"], alg[f"{kernel}_flops"]
+    hbm = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    mfma = flops / nbytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    inst = "gate/up + SwiGLU" if kernel == "gate_up" else "down"
+    return {"kernel": f"beam::stream_gemm_kernel, {inst} instance",
+            "bound": "mfma" if mfma else "hbm",
+            "achieved": round(tf if mfma else hbm, 1),
+            "peak": BF16_PEAK_TFLOPS if mfma else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma else "GB/s",
+            "frac": round((tf / BF16_PEAK_TFLOPS) if mfma else (hbm / HBM_PEAK_GBS), 4),
+            "traffic": measured_traffic(kernel) if workload == "prefill" else None,
+            "bytes_per_launch": nbytes, "flops_per_launch": flops,
+            "avg_launch_ms": round(ms, 4), "hbm_gbs": round(hbm, 1), "tflops": round(tf, 1)}
 
 
 def main():
@@ -301,7 +413,6 @@ def main():
     alg = algorithmic(w, r["counts"])
     ms = r["ms_per_step"]
     gu_ms = r["stage_ms"]["gate_up"]
-    gu_gbs = alg["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9
     layer_gbs = alg["layer_bytes"] / (ms * 1e-3) / 1e9
     mfma_frac = alg["expert_flops"] / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
     c = r["counts"]
@@ -318,11 +429,8 @@ def main():
                                f"groups={w.G} kept={w.KG} topk={w.K}",
                    "tokens": w.T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
                    "seed": args.seed},
-        "roofline": {"kernel": "beam::stream_gemm_kernel, gate/up + SwiGLU instance", "bound": "hbm",
-                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if w.name == "prefill" else None,
-                     "bytes_per_launch": alg["gate_up_bytes"], "avg_launch_ms": round(gu_ms, 4)},
+        "roofline": kernel_roofline("gate_up", alg, r["stage_ms"], w.name),
+        "roofline_down": kernel_roofline("down", alg, r["stage_ms"], w.name),
         "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                   "roofline_frac": round(max(layer_gbs / HBM_PEAK_GBS, mfma_frac), 4),
                   "device_step_ms": {k: round(v, 4) for k, v in r["device_step_ms"].items()},
@@ -371,7 +479,26 @@ def main():
                             "hbm_frac": round(da["layer_bytes"] / (d["ms_per_step"] * 1e-3) / 1e9
                                               / HBM_PEAK_GBS, 4),
                             "touched_experts": da["touched"],
-                            "stage_ms": {k: round(v, 4) for k, v in d["stage_ms"].items()}}
+                            "stage_ms": {k: round(v, 4) for k, v in d["stage_ms"].items()},
+                            "roofline_gate_up": kernel_roofline("gate_up", da, d["stage_ms"], "decode")}
+        if not args.no_parity:
+            print("[bench] decode parity against the oracle", file=sys.stderr, flush=True)
+            result["decode"]["parity"] = layer_parity(d["w"], d["x"], d["out"], d["ids"], wts)
+        # the touched-expert count (and so the bytes streamed) varies with the
+        # draw: the same batch size at other seeds
+        per_seed = []
+        for sd in range(args.seed + 1, args.seed + args.decode_seeds):
+            ds = run_workload("decode", wts, args, max(args.steps, 10), 3, gtr, synth, torch,
+                              seed=sd, layer_ref=False)
+            dsa = algorithmic(ds["w"], ds["counts"])
+            t_s = ds["ms_per_step"] * 1e-3
+            per_seed.append({"seed": sd, "touched_experts": dsa["touched"],
+                             "ms_per_step": round(ds["ms_per_step"], 4),
+                             "tokens_per_s": round(ds["w"].T / t_s, 1),
+                             "hbm_frac": round(dsa["layer_bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4)})
+            del ds
+        if per_seed:
+            result["decode"]["other_seeds"] = per_seed
         del d
     if not args.no_other_workloads:
         # the other shapes of the layer's operating range: a 512-token batch
@@ -393,7 +520,19 @@ def main():
                                            oa["expert_flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t_s, 4),
                 "touched_experts": oa["touched"],
                 "max_rows_per_expert": int(o["counts"].max()),
+                "histogram": {"max": int(o["counts"].max()), "min": int(o["counts"].min()),
+                              "lt10": int((o["counts"] < 10).sum()),
+                              "empty": int((o["counts"] == 0).sum())},
+                "roofline_gate_up": kernel_roofline("gate_up", oa, o["stage_ms"], name),
+                "roofline_down": kernel_roofline("down", oa, o["stage_ms"], name),
                 "stage_ms": {k: round(v, 4) for k, v in o["stage_ms"].items()}}
+            if not args.no_parity:
+                # every token of the 512-token batch; 1024 sampled tokens of the
+                # 16K-token one (its routing is still checked for every token)
+                print(f"[bench] {name} parity against the oracle", file=sys.stderr, flush=True)
+                result["other_workloads"][name]["parity"] = layer_parity(
+                    o["w"], o["x"], o["out"], o["ids"], wts,
+                    sample=None if o["w"].T <= 4096 else 1024, seed=args.seed)
             del o
     if not args.no_fp8:
         # the FP8 per-channel variant of the same layer (weights quantised once
@@ -460,6 +599,17 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, r["x"], wts, args.cpu_experts, torch,
                                               gpu_out=r["out"], gpu_ids=r["ids"])
+    # the benchmark spec layer-output statistics of every workload in one place
+    par = {}
+    if result.get("decode", {}).get("parity"):
+        par["decode"] = result["decode"]["parity"]
+    for name, o in result.get("other_workloads", {}).items():
+        if o.get("parity"):
+            par[name] = o["parity"]
+    if result.get("cpu_baseline", {}).get("parity"):
+        par[w.name] = result["cpu_baseline"]["parity"]
+    if par:
+        result["parity"] = par
     print(json.dumps(result), flush=True)
 
 

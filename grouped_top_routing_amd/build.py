@@ -66,9 +66,35 @@ def build(verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"link failed ({r.returncode}):\n{_filtered(r.stdout + r.stderr)}")
         os.replace(tmp, LIB)
+        _write_build_info()
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
+
+
+def _write_build_info() -> None:
+    """Records, next to the library, the commit it was built from and whether
+    the tree had uncommitted changes (a copy of the tree without .git can
+    still name its build)."""
+    import hashlib
+    import json
+    root = os.path.dirname(PKG)
+    info = {"git": None, "dirty": None,
+            "sources_sha256": hashlib.sha256(b"".join(
+                open(os.path.join(CSRC, f), "rb").read() for f in sorted(os.listdir(CSRC))
+            )).hexdigest()}
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=root,
+                             capture_output=True, text=True, timeout=10)
+        if sha.returncode == 0:
+            info["git"] = sha.stdout.strip()
+            st = subprocess.run(["git", "status", "--porcelain", "--untracked-files=no"],
+                                cwd=root, capture_output=True, text=True, timeout=10)
+            info["dirty"] = bool(st.stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(PKG, "_build_info.json"), "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":
