@@ -166,7 +166,7 @@ int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const
                                         (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0,
                                         c->weight_layout, lora,
                                         max_tiles * (H / ffn_out_cols_per_item(false)), s,
-                                        false));
+                                        ffn_stream_weights(pairs(c), c->num_experts)));
 }
 
 int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const int32_t* offsets,

@@ -8,6 +8,13 @@ namespace beam {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// Fourth word of a raw (stride 0, untyped) buffer descriptor on gfx9-family
+// GPUs: DATA_FORMAT = 32 bits (a zero format would make every access out of
+// range).  Accesses at offsets at or past the descriptor's byte count are
+// dropped by the hardware: stores do nothing, loads return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 constexpr int kWave = 64;
 
@@ -21,6 +28,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Two fp32 values rounded to bf16 (round-to-nearest-even, as f32_to_bf16
+// for every non-NaN input) and packed, lo in the low half: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // 16-byte global load / store.

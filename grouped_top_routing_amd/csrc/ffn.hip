@@ -64,6 +64,15 @@ namespace beam {
 #ifndef BEAM_GEMM_MAXMB
 #define BEAM_GEMM_MAXMB 12
 #endif
+#ifndef BEAM_GEMM_MB16
+#define BEAM_GEMM_MB16 1
+#endif
+#ifndef BEAM_GEMM_S16
+#define BEAM_GEMM_S16 3
+#endif
+#ifndef BEAM_GEMM_DOWN_NT
+#define BEAM_GEMM_DOWN_NT 0
+#endif
 #ifndef BEAM_GEMM_NW8
 #define BEAM_GEMM_NW8 8
 #endif
@@ -145,6 +154,41 @@ constexpr int ring_bytes() {
                       : S * (kItemBlocks + MB) * kFrag;
 }
 
+// Source rows of this wave's A loads in the 128/192-row configurations: for
+// each of its row blocks j (block wave + kNW j of the m-tile) and half hf,
+// lane l reads tile row 16 (wave + kNW j) + 8 hf + l / 8 (rows past the tile
+// repeat its last row), i.e. row gather[row0 + that] / topk of A (or row0 +
+// that without a gather).  The gather indices are read with scalar loads of
+// uniform addresses: those are counted in lgkmcnt, never in the vector memory
+// counter that the direct-load ring is waited on with, so reading them does
+// not drain loads in flight.
+template <int AM, int kNW>
+__device__ __forceinline__ void paired_a_rows(int (&rows)[AM][2], const int32_t* gather, int topk,
+                                              int row0, int nrows, int wave, int lane) {
+  const int sel = lane >> 3;
+#pragma unroll
+  for (int j = 0; j < AM; ++j) {
+    const int blk = __builtin_amdgcn_readfirstlane((wave + kNW * j) * 16);
+    if (gather) {
+      const __attribute__((address_space(4))) int32_t* cg =
+          (const __attribute__((address_space(4))) int32_t*)gather;
+      int v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = cg[row0 + min(blk + k, nrows - 1)];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int x = v[8 * hf];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) x = sel == k ? v[8 * hf + k] : x;
+        rows[j][hf] = x / topk;
+      }
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) rows[j][hf] = row0 + min(blk + 8 * hf + sel, nrows - 1);
+    }
+  }
+}
+
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
 // this wave computes RB blocks starting at block row_off.  MB sizes the LDS
 // ring; fragments of blocks NRB..MB-1 are not loaded.
@@ -192,14 +236,14 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // (the 192-row configuration has no registers to spare).
   constexpr int NHF = kPairA ? 2 : 1;
   int asrow[AMAX > 0 ? AMAX : 1][NHF];
+  if constexpr (kPairA) {
+    paired_a_rows<(AMAX > 0 ? AMAX : 1), kNW>(asrow, a.gather, a.topk, a.row0, a.nrows, wave, lane);
+  } else {
 #pragma unroll
-  for (int j = 0; j < AMAX; ++j) {
-#pragma unroll
-    for (int hf = 0; hf < NHF; ++hf) {
-      const int rho = kPairA ? hf * 8 + (lane >> 3) : r;
-      int row = (wave + kNW * j) * 16 + rho;
+    for (int j = 0; j < AMAX; ++j) {
+      int row = (wave + kNW * j) * 16 + r;
       row = row < a.nrows ? row : a.nrows - 1;  // rows past the tile repeat its last row
-      asrow[j][hf] = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
+      asrow[j][0] = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
     }
   }
   auto asrc = [&](int j, int hf, int k0) {
@@ -502,30 +546,38 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // leave as one 8-byte store (four bf16); the column blocks of one row are
   // written by neighbouring lanes and waves in the same few instructions and
   // merge into whole lines in L2.
+  // The stores are range-checked buffer stores over this m-tile's output
+  // rows: a lane whose row lies past the tile gets an offset outside the
+  // range and its store is dropped (no branch around the stores), and the
+  // four values are rounded to bf16 and packed in pairs by the hardware
+  // conversion.
   if constexpr (RB > 0) {
-    uint16_t* out = a.C + (size_t)a.row0 * a.n_out + a.ntile * WCOLS;
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+        a.C + (size_t)a.row0 * a.n_out, 0, a.nrows * a.n_out * 2, kBufferRsrcWord3);
+    // the lane's row and column, opaque to the optimiser so that the store
+    // offsets are formed here rather than kept live (or spilled) across the
+    // k loop
+    int er = r, eg = g;
+    asm volatile("" : "+v"(er), "+v"(eg));
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int row = (row_off + i) * 16 + r;
-      if (row < a.nrows) {
+      const int row = (row_off + i) * 16 + er;
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-          uint32_t h[4];
+      for (int j = 0; j < HALF; ++j) {
+        float o[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float o;
-            if (SWIGLU) {
-              const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
-              o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
-            } else {
-              o = acc[i][j][v];
-            }
-            h[v] = f32_to_bf16(o);
+        for (int v = 0; v < 4; ++v) {
+          if (SWIGLU) {
+            const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
+            o[v] = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+          } else {
+            o[v] = acc[i][j][v];
           }
-          const int col = cg * HALF * 16 + j * 16 + 4 * g;
-          *reinterpret_cast<uint2*>(out + (size_t)row * a.n_out + col) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
+        const int col = a.ntile * WCOLS + cg * HALF * 16 + j * 16 + 4 * eg;
+        const uint32_t off = row < a.nrows ? (uint32_t)(row * a.n_out + col) * 2u : 0x80000000u;
+        const u32x2_t d = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(d, out, off, 0, 0);
       }
     }
   }
@@ -708,6 +760,7 @@ int ffn_choose_mb(int64_t rows, int E) {
   const int64_t mean = rows / (E > 0 ? E : 1);
   if (mean <= 40) return 4;
   if (mean <= 80 || BEAM_GEMM_MAXMB == 8) return 8;
+  if (BEAM_GEMM_MB16 && mean > 160) return 16;
   return BEAM_GEMM_MAXMB;
 }
 
@@ -760,10 +813,20 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
       if (swiglu && stream_weights)
         return launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12, BEAM_GEMM_S12, true,
                              false, true>(BEAM_STREAM_ARGS);
+#if BEAM_GEMM_DOWN_NT
+      if (!swiglu && stream_weights)
+        return launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12, BEAM_GEMM_S12, false,
+                             false, true>(BEAM_STREAM_ARGS);
+#endif
       return swiglu ? launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12,
                                     BEAM_GEMM_S12, true>(BEAM_STREAM_ARGS)
                     : launch_stream<BEAM_GEMM_MAXMB, BEAM_GEMM_NW12, BEAM_GEMM_RG12,
                                     BEAM_GEMM_S12, false>(BEAM_STREAM_ARGS);
+#endif
+#if BEAM_GEMM_MB16
+    case 16:
+      return swiglu ? launch_stream<16, 8, 2, BEAM_GEMM_S16, true, false, false>(BEAM_STREAM_ARGS)
+                    : launch_stream<16, 8, 2, BEAM_GEMM_S16, false, false, false>(BEAM_STREAM_ARGS);
 #endif
     default:
       return hipErrorInvalidValue;

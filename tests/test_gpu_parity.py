@@ -179,9 +179,10 @@ def test_expert_ffn_ragged_tiles(tiny, hot_rows, T):
     # one expert gets `hot_rows` rows, the rest spread thinly: m-tiles with
     # ragged tails, experts with a single row, and every m-tile height the
     # library picks from the mean rows per expert (up to 1024 tokens -> 64-row
-    # tiles, 2048 -> 128, 3072 and up -> 192; at 16384 tokens there are ~3
-    # times more m-tiles than workgroups, so each workgroup runs several items
-    # back to back and starts each next item's weight stream early)
+    # tiles, 2048 -> 128, 3072 and 4096 -> 192, above 5120 -> 256; at 16384
+    # tokens there are more m-tiles than workgroups, so each workgroup runs
+    # several items back to back and starts each next item's weight stream
+    # early)
     say(f"[expert_ffn] ragged hot_rows={hot_rows} T={T}")
     npd = tiny["np"]
     rng = np.random.default_rng(hot_rows)
@@ -357,14 +358,14 @@ def test_layer_replays_from_a_captured_graph(tiny, variant):
 
 # -------------------------------------------------------- grid independence
 @pytest.mark.parametrize("variant,T", [("bf16", 128), ("bf16", 2048), ("bf16", 4096),
-                                       ("fp8", 64), ("fp8", 2048), ("fp8", 4096),
-                                       ("lora", 4096)])
+                                       ("bf16", 8192), ("fp8", 64), ("fp8", 2048),
+                                       ("fp8", 4096), ("lora", 4096), ("lora", 8192)])
 def test_layer_independent_of_grid_size(tiny, variant, T, monkeypatch):
     # each work item is computed whole by one workgroup, so capping the
     # persistent GEMM grid must not change a bit; with 8 workgroups every
     # workgroup runs a long chain of items (each starting the next one's
     # weight stream early) at every m-tile height (T 64..128 -> 32/64 rows,
-    # 2048 -> 128, 4096 -> 192)
+    # 2048 -> 128, 4096 -> 192, 8192 -> 256 for bf16 and LoRA)
     say(f"[grid] {variant} T={T}")
     wr, wgu, wd = tiny["w_router"], tiny["w_gate_up"], tiny["w_down"]
     f8 = gtr.quantize_fp8(wgu, wd) if variant == "fp8" else None
@@ -420,7 +421,7 @@ def test_expert_ffn_random_batches(tiny, seed):
 
 # ---------------------------------------------------- other supported shapes
 @pytest.mark.parametrize("H,I", [(512, 384), (768, 640)])
-@pytest.mark.parametrize("T", [96, 2048, 4096])
+@pytest.mark.parametrize("T", [96, 2048, 4096, 8192])
 def test_expert_paths_other_shapes(H, I, T):
     # hidden and intermediate sizes other than the tiny and Beam ones (I not a
     # multiple of 256: odd 64-k stage counts, 3 or 5 n-tiles per m-tile) at
