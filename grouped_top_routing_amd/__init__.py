@@ -17,4 +17,5 @@ from ._lib import (  # noqa: F401
     expert_gate_up, expert_gate_up_fp8, layer_forward, layer_forward_fp8,
     layer_forward_noalloc, lib, make_config,
     pack_weights, permute, quantize_fp8, route, route_replay, status_string, workspace_bytes,
+    LIB_CHECKED_PATH, CHECK_BITS, check_flags, use_library,
 )

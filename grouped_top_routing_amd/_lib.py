@@ -14,6 +14,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbeam_moe.so")
+#: the debug build with the kernels' index checks (include/beam_moe_debug.h)
+LIB_CHECKED_PATH = os.path.join(_PKG, "libbeam_moe_checked.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -21,6 +23,11 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_ERR_TOO_LARGE = -5
+
+#: check bits of the debug build (include/beam_moe_debug.h)
+CHECK_BITS = {"permute_row": 1 << 0, "plan_capacity": 1 << 1, "plan_rows": 1 << 2,
+              "gather_index": 1 << 3, "token_index": 1 << 4, "weight_offset": 1 << 5,
+              "combine_row": 1 << 6}
 
 ENTRY_ROUTE = 0
 ENTRY_PERMUTE = 1
@@ -40,7 +47,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_route_replay", "moe_permute"
            "moe_layer_forward", "moe_pack_weights", "moe_quantize_fp8", "moe_expert_ffn_fp8",
            "moe_expert_gate_up_fp8", "moe_expert_down_fp8", "moe_layer_forward_fp8",
            "moe_expert_ffn_lora", "moe_layer_forward_lora", "moe_layer_forward_noalloc",
-           "moe_status_string")
+           "moe_debug_check_flags", "moe_status_string")
 
 
 class MoeConfig(ctypes.Structure):
@@ -82,38 +89,72 @@ def lib() -> ctypes.CDLL:
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m grouped_top_routing_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        CP = ctypes.POINTER(MoeConfig)
-        L.moe_workspace_bytes.argtypes = [CP, I, ctypes.POINTER(Z)]
-        L.moe_route.argtypes = [CP, P, P, P, P, P, P, Z, P]
-        L.moe_route_replay.argtypes = [CP, P, P, P, P, P, Z, P]
-        L.moe_permute.argtypes = [CP, P, P, P, P, P, P, Z, P]
-        L.moe_expert_ffn.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
-        L.moe_expert_gate_up.argtypes = [CP, P, P, P, P, P, P, Z, P]
-        L.moe_expert_down.argtypes = [CP, P, P, P, P, P, Z, P]
-        L.moe_combine.argtypes = [CP, P, P, P, P, P]
-        L.moe_pack_weights.argtypes = [CP, P, P, P, P, P]
-        L.moe_layer_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
-        L.moe_layer_forward_noalloc.argtypes = [CP, P, P, P, P, P, P, P, P, P]
-        L.moe_quantize_fp8.argtypes = [CP, P, P, P, P, P, P, P]
-        L.moe_expert_ffn_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
-        L.moe_expert_gate_up_fp8.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
-        L.moe_expert_down_fp8.argtypes = [CP, P, P, P, P, P, P, Z, P]
-        L.moe_layer_forward_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, Z, P]
-        LP = ctypes.POINTER(MoeLora)
-        L.moe_expert_ffn_lora.argtypes = [CP, P, P, P, P, P, LP, P, P, Z, P]
-        L.moe_layer_forward_lora.argtypes = [CP, P, P, P, P, P, LP, P, P, P, P, Z, P]
-        L.moe_status_string.argtypes = [I]
-        L.moe_status_string.restype = ctypes.c_char_p
-        for name in EXPORTS:
-            if name != "moe_status_string":
-                getattr(L, name).restype = I
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Loads one build of the library (normal or checked) with its argument
+    types declared (raises if it is missing)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m grouped_top_routing_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    CP = ctypes.POINTER(MoeConfig)
+    L.moe_workspace_bytes.argtypes = [CP, I, ctypes.POINTER(Z)]
+    L.moe_route.argtypes = [CP, P, P, P, P, P, P, Z, P]
+    L.moe_route_replay.argtypes = [CP, P, P, P, P, P, Z, P]
+    L.moe_permute.argtypes = [CP, P, P, P, P, P, P, Z, P]
+    L.moe_expert_ffn.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
+    L.moe_expert_gate_up.argtypes = [CP, P, P, P, P, P, P, Z, P]
+    L.moe_expert_down.argtypes = [CP, P, P, P, P, P, Z, P]
+    L.moe_combine.argtypes = [CP, P, P, P, P, P]
+    L.moe_pack_weights.argtypes = [CP, P, P, P, P, P]
+    L.moe_layer_forward.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
+    L.moe_layer_forward_noalloc.argtypes = [CP, P, P, P, P, P, P, P, P, P]
+    L.moe_quantize_fp8.argtypes = [CP, P, P, P, P, P, P, P]
+    L.moe_expert_ffn_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, Z, P]
+    L.moe_expert_gate_up_fp8.argtypes = [CP, P, P, P, P, P, P, P, Z, P]
+    L.moe_expert_down_fp8.argtypes = [CP, P, P, P, P, P, P, Z, P]
+    L.moe_layer_forward_fp8.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    LP = ctypes.POINTER(MoeLora)
+    L.moe_expert_ffn_lora.argtypes = [CP, P, P, P, P, P, LP, P, P, Z, P]
+    L.moe_layer_forward_lora.argtypes = [CP, P, P, P, P, P, LP, P, P, P, P, Z, P]
+    L.moe_debug_check_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+    L.moe_status_string.argtypes = [I]
+    L.moe_status_string.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name != "moe_status_string":
+            getattr(L, name).restype = I
+    return L
+
+
+class use_library:
+    """Context manager: the binding's calls go to another build of the
+    library (e.g. the checked one) inside the block."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = lib()
+        _lib = load(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def check_flags() -> dict:
+    """moe_debug_check_flags of the library in use: {check name: bool} of the
+    bits recorded since the last call (the checked build only)."""
+    f = ctypes.c_uint32(0)
+    _call("moe_debug_check_flags", lib().moe_debug_check_flags(ctypes.byref(f)))
+    return {k: bool(f.value & b) for k, b in CHECK_BITS.items()}
 
 
 def status_string(code: int) -> str:

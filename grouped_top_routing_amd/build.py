@@ -1,6 +1,7 @@
 """Builds libbeam_moe.so in-tree with hipcc for gfx950.
 
-Usage: python -m grouped_top_routing_amd.build   (or call build()).
+Usage: python -m grouped_top_routing_amd.build [--normal | --checked | --sanitized]
+(all three libraries by default; or call build() / build_all()).
 """
 from __future__ import annotations
 
@@ -13,6 +14,21 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbeam_moe.so")
+# the debug build: kernels verify their derived indices (include/beam_moe_debug.h)
+LIB_CHECKED = os.path.join(PKG, "libbeam_moe_checked.so")
+# host code built with AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is the normal build's), for running the C ABI's host-side
+# validation under the sanitizers
+LIB_SANITIZED = os.path.join(PKG, "libbeam_moe_sanitized.so")
+
+
+def clang_rt_dir() -> str:
+    """Directory of the clang sanitizer runtimes that LIB_SANITIZED needs."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang's AddressSanitizer runtime was not found under /opt/rocm")
+    return os.path.dirname(hits[-1])
 SOURCES = ["capi.hip", "route.hip", "permute.hip", "ffn.hip", "ffn_fp8.hip", "lora.hip", "combine.hip"]
 ARCH = "gfx950"
 
@@ -36,16 +52,24 @@ def _filtered(text: str) -> str:
     return "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, checked: bool = False, sanitized: bool = False) -> str:
     """Compile every HIP source (one hipcc process per file, in parallel) and
-    link them into one shared library; returns its path."""
+    link them into one shared library; returns its path.  checked: the debug
+    library with the kernels' index checks (BEAM_MOE_CHECKED=1); sanitized:
+    host code under AddressSanitizer and UndefinedBehaviorSanitizer."""
     cc = hipcc()
+    lib = LIB_CHECKED if checked else LIB_SANITIZED if sanitized else LIB
+    extra = ["-DBEAM_MOE_CHECKED=1"] if checked else []
+    if sanitized:
+        # each sanitizer flag applies to the host compilation only
+        extra = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
     tmpdir = tempfile.mkdtemp(prefix="beam_moe_build_")
     try:
         procs = []
         for s in SOURCES:
             obj = os.path.join(tmpdir, s.replace(".hip", ".o"))
-            cmd = [cc, *_flags(), "-c", os.path.join(CSRC, s), "-o", obj]
+            cmd = [cc, *_flags(), *extra, "-c", os.path.join(CSRC, s), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((s, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -59,17 +83,33 @@ def build(verbose: bool = False) -> str:
                 print(out)
         if errors:
             raise RuntimeError("\n".join(errors))
-        tmp = LIB + ".tmp"
+        tmp = lib + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o, _ in procs],
                "-o", tmp]
+        if sanitized:
+            # the host link with the shared sanitizer runtimes
+            cmd = [os.path.join(os.path.dirname(cc), "..", "llvm", "bin", "clang++"), "-shared",
+                   "-fPIC", "-fsanitize=address,undefined", "-shared-libasan",
+                   *[o for _, o, _ in procs], "-L/opt/rocm/lib", "-lamdhip64",
+                   "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed ({r.returncode}):\n{_filtered(r.stdout + r.stderr)}")
-        os.replace(tmp, LIB)
-        _write_build_info()
+        os.replace(tmp, lib)
+        if not checked and not sanitized:
+            _write_build_info()
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB
+    return lib
+
+
+def build_all(verbose: bool = False) -> list:
+    """The three libraries (normal, checked, sanitized), compiled concurrently."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(3) as pool:
+        futs = [pool.submit(build, verbose, c, z) for c, z in ((False, False), (True, False),
+                                                                 (False, True))]
+        return [f.result() for f in futs]
 
 
 def _write_build_info() -> None:
@@ -98,4 +138,11 @@ def _write_build_info() -> None:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--checked" in sys.argv:
+        print(build(verbose="-v" in sys.argv, checked=True))
+    elif "--sanitized" in sys.argv:
+        print(build(verbose="-v" in sys.argv, sanitized=True))
+    elif "--normal" in sys.argv:
+        print(build(verbose="-v" in sys.argv))
+    else:
+        print("\n".join(build_all(verbose="-v" in sys.argv)))

@@ -7,6 +7,8 @@
 #include <mutex>
 
 #include "../../include/beam_moe.h"
+#include "../../include/beam_moe_debug.h"
+#include "common.h"
 #include "kernels.h"
 
 namespace {
@@ -146,6 +148,16 @@ int do_plan(const moe_config_t* c, const int32_t* offsets, int32_t* plan, int mb
                                      (int)max_tiles_for(c), s));
 }
 
+// the sizes the checked build verifies the GEMMs' indices against: permuted
+// rows, rows of A (tokens for gate/up, permuted rows for down), experts
+GemmBounds bounds_of(const moe_config_t* c, bool gate_up) {
+  GemmBounds b;
+  b.n_rows = pairs(c);
+  b.n_src = gate_up ? c->num_tokens : pairs(c);
+  b.n_experts = c->num_experts;
+  return b;
+}
+
 int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
                const int32_t* plan, const uint16_t* wgu, uint16_t* h, hipStream_t s,
                const LoraArgs& lora = LoraArgs{}) {
@@ -155,7 +167,8 @@ int do_gate_up(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
                                         (int64_t)2 * I * H, h, plan, (int)max_tiles, H, I, I,
                                         c->weight_layout, lora,
                                         max_tiles * (I / ffn_out_cols_per_item(true)), s,
-                                        ffn_stream_weights(pairs(c), c->num_experts)));
+                                        ffn_stream_weights(pairs(c), c->num_experts),
+                                        bounds_of(c, true)));
 }
 
 int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint16_t* wd,
@@ -166,7 +179,8 @@ int do_down(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const
                                         (int64_t)H * I, y, plan, (int)max_tiles, I, H, 0,
                                         c->weight_layout, lora,
                                         max_tiles * (H / ffn_out_cols_per_item(false)), s,
-                                        ffn_stream_weights(pairs(c), c->num_experts)));
+                                        ffn_stream_weights(pairs(c), c->num_experts),
+                                        bounds_of(c, false)));
 }
 
 int do_ffn(const moe_config_t* c, const uint16_t* x, const int32_t* psrc, const int32_t* offsets,
@@ -232,7 +246,7 @@ int do_gate_up_fp8(const moe_config_t* c, const uint16_t* x, const int32_t* psrc
   return hip_status(launch_grouped_gemm_fp8(mb_for_fp8(c), true, x, psrc, c->topk, q, sc,
                                             (int64_t)2 * I * H, 2 * I, h, plan, (int)max_tiles, H,
                                             I, I, max_tiles * (I / ffn_out_cols_per_item(true)),
-                                            s));
+                                            s, bounds_of(c, true)));
 }
 
 int do_down_fp8(const moe_config_t* c, const uint16_t* h, const int32_t* plan, const uint8_t* q,
@@ -241,7 +255,8 @@ int do_down_fp8(const moe_config_t* c, const uint16_t* h, const int32_t* plan, c
   const int H = c->hidden, I = c->intermediate;
   return hip_status(launch_grouped_gemm_fp8(mb_for_fp8(c), false, h, nullptr, c->topk, q, sc,
                                             (int64_t)H * I, H, y, plan, (int)max_tiles, I, H, 0,
-                                            max_tiles * (H / ffn_out_cols_per_item(false)), s));
+                                            max_tiles * (H / ffn_out_cols_per_item(false)), s,
+                                            bounds_of(c, false)));
 }
 
 int do_ffn_fp8(const moe_config_t* c, const uint16_t* x, const int32_t* psrc,
@@ -529,6 +544,19 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
                       [&](const int32_t* psrc, const int32_t* offsets, uint16_t* y, void* scratch) {
                         return do_ffn(cfg, x, psrc, offsets, w_gate_up, w_down, y, scratch, s);
                       });
+}
+
+int moe_debug_check_flags(uint32_t* flags) {
+  if (!flags) return MOE_ERR_INVALID_ARG;
+  *flags = 0;
+#if BEAM_MOE_CHECKED
+  if (device_ready()) return MOE_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+  *flags = check_flags_permute() | check_flags_ffn() | check_flags_combine();
+  return MOE_OK;
+#else
+  return MOE_ERR_UNSUPPORTED;
+#endif
 }
 
 int moe_layer_forward_noalloc(const moe_config_t* cfg, const uint16_t* x, const float* w_router,

@@ -29,6 +29,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     rows[j] = j < topk ? perm_dst[(size_t)t * topk + j] : -1;
+    if (rows[j] >= 0)
+      rows[j] = BEAM_CLAMP(rows[j], 0, (int64_t)gridDim.x * topk - 1, kCheckCombineRow);
     wt[j] = j < topk ? w[(size_t)t * topk + j] : 0.f;
   }
   for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
@@ -57,6 +59,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     st16(out + (size_t)t * H + 8 * v, make_uint4(o[0], o[1], o[2], o[3]));
   }
 }
+
+BEAM_DEFINE_CHECK_READER(check_flags_combine)
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
                           uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream) {

@@ -62,6 +62,57 @@ __device__ __forceinline__ float sigmoidf_(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// Checked builds (BEAM_MOE_CHECKED=1, the debug library).  Kernels verify the
+// indices they derive from their inputs before using them; a failing check
+// sets its bit in the translation unit's flag word and clamps the index into
+// range, so no access leaves its buffer and no load is skipped (the expert
+// GEMMs' wait counts stay exact).  The host reads and clears the words with
+// moe_debug_check_flags.  In the normal build the checks compile to nothing.
+enum CheckBit : uint32_t {
+  kCheckPermuteRow = 1u << 0,     // permutation row outside [0, pairs)
+  kCheckPlanCapacity = 1u << 1,   // more m-tiles than the plan holds
+  kCheckPlanRows = 1u << 2,       // m-tile rows outside [0, pairs) or bad expert
+  kCheckGatherIndex = 1u << 3,    // gathered pair index outside [0, pairs)
+  kCheckTokenIndex = 1u << 4,     // A row (token) outside the activations
+  kCheckWeightOffset = 1u << 5,   // weight stage or row block outside the expert
+  kCheckCombineRow = 1u << 6,     // combine row outside [0, pairs)
+};
+#ifndef BEAM_MOE_CHECKED
+#define BEAM_MOE_CHECKED 0
+#endif
+#if BEAM_MOE_CHECKED
+static __device__ uint32_t g_check_flags;  // one word per translation unit
+// v if lo <= v <= hi; else records `bit` and returns v clamped into [lo, hi]
+template <class T>
+__device__ __forceinline__ T check_clamp(T v, int64_t lo, int64_t hi, uint32_t bit) {
+  if ((int64_t)v < lo || (int64_t)v > hi) {
+    atomicOr(&g_check_flags, bit);
+    return (T)((int64_t)v < lo ? lo : hi);
+  }
+  return v;
+}
+__device__ __forceinline__ void check_that(bool ok, uint32_t bit) {
+  if (!ok) atomicOr(&g_check_flags, bit);
+}
+#define BEAM_CLAMP(v, lo, hi, bit) (::beam::check_clamp((v), (lo), (hi), (bit)))
+#define BEAM_CHECK(ok, bit) ::beam::check_that((ok), (bit))
+// Host side: this translation unit's flag word, read and cleared (0 when the
+// device call fails).
+#define BEAM_DEFINE_CHECK_READER(fn)                                          \
+  uint32_t fn() {                                                              \
+    uint32_t v = 0, zero = 0;                                                  \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_flags), sizeof v) != hipSuccess) return 0; \
+    (void)hipMemcpyToSymbol(HIP_SYMBOL(g_check_flags), &zero, sizeof zero);    \
+    return v;                                                                  \
+  }
+#else
+#define BEAM_CLAMP(v, lo, hi, bit) (v)
+#define BEAM_CHECK(ok, bit) ((void)0)
+#define BEAM_DEFINE_CHECK_READER(fn) \
+  uint32_t fn() { return 0; }
+#endif
+
+// ---------------------------------------------------------------------------
 // Direct global -> LDS streaming (used by the expert GEMMs and the router).
 // s_waitcnt immediate (GFX9 encoding) that waits until at most n vector
 // memory operations of this wave are outstanding; other counters untouched.

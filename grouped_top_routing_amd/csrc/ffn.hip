@@ -119,6 +119,8 @@ struct ItemArgs {
   int64_t w_expert_stride;
   const int32_t* plan_expert;
   int q, grid, total, nt_n;
+  // checked builds: permuted rows and rows of A the indices must stay below
+  int64_t n_rows, n_src;
   // fp8 weights: this expert's fp32 scale per weight row (W then holds the
   // E4M3FN codes in the fp8 fragment layout); null for bf16 weights
   const float* scale;
@@ -164,7 +166,10 @@ constexpr int ring_bytes() {
 // not drain loads in flight.
 template <int AM, int kNW>
 __device__ __forceinline__ void paired_a_rows(int (&rows)[AM][2], const int32_t* gather, int topk,
-                                              int row0, int nrows, int wave, int lane) {
+                                              int row0, int nrows, int wave, int lane,
+                                              int64_t n_rows, int64_t n_src) {
+  (void)n_rows;
+  (void)n_src;
   const int sel = lane >> 3;
 #pragma unroll
   for (int j = 0; j < AM; ++j) {
@@ -174,17 +179,20 @@ __device__ __forceinline__ void paired_a_rows(int (&rows)[AM][2], const int32_t*
           (const __attribute__((address_space(4))) int32_t*)gather;
       int v[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = cg[row0 + min(blk + k, nrows - 1)];
+      for (int k = 0; k < 16; ++k)
+        v[k] = cg[BEAM_CLAMP(row0 + min(blk + k, nrows - 1), 0, n_rows - 1, kCheckGatherIndex)];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         int x = v[8 * hf];
 #pragma unroll
         for (int k = 1; k < 8; ++k) x = sel == k ? v[8 * hf + k] : x;
-        rows[j][hf] = x / topk;
+        rows[j][hf] = BEAM_CLAMP(x / topk, 0, n_src - 1, kCheckTokenIndex);
       }
     } else {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) rows[j][hf] = row0 + min(blk + 8 * hf + sel, nrows - 1);
+      for (int hf = 0; hf < 2; ++hf)
+        rows[j][hf] = BEAM_CLAMP(row0 + min(blk + 8 * hf + sel, nrows - 1), 0, n_src - 1,
+                                 kCheckTokenIndex);
     }
   }
 }
@@ -237,13 +245,17 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int NHF = kPairA ? 2 : 1;
   int asrow[AMAX > 0 ? AMAX : 1][NHF];
   if constexpr (kPairA) {
-    paired_a_rows<(AMAX > 0 ? AMAX : 1), kNW>(asrow, a.gather, a.topk, a.row0, a.nrows, wave, lane);
+    paired_a_rows<(AMAX > 0 ? AMAX : 1), kNW>(asrow, a.gather, a.topk, a.row0, a.nrows, wave, lane,
+                                              a.n_rows, a.n_src);
   } else {
 #pragma unroll
     for (int j = 0; j < AMAX; ++j) {
       int row = (wave + kNW * j) * 16 + r;
       row = row < a.nrows ? row : a.nrows - 1;  // rows past the tile repeat its last row
-      asrow[j][0] = a.gather ? a.gather[a.row0 + row] / a.topk : a.row0 + row;
+      asrow[j][0] = a.gather
+          ? a.gather[BEAM_CLAMP(a.row0 + row, 0, a.n_rows - 1, kCheckGatherIndex)] / a.topk
+          : a.row0 + row;
+      asrow[j][0] = BEAM_CLAMP(asrow[j][0], 0, a.n_src - 1, kCheckTokenIndex);
     }
   }
   auto asrc = [&](int j, int hf, int k0) {
@@ -266,7 +278,9 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // this lane's 16 bytes at lane*16, and a row block's fragments follow each
   // other along k (bf16: one per 32 k; fp8: one per 64 k).
   auto bbase_of = [&](const uint16_t* W, int ntile, int t) -> const uint8_t* {
-    const int wrow0 = weight_row_of(rg + RG * t, ntile) - r;  // uniform
+    // uniform; the block's 16 rows lie inside the expert's weight rows
+    const int wrow0 = BEAM_CLAMP(weight_row_of(rg + RG * t, ntile) - r, 0,
+                                 (SWIGLU ? a.up_row0 : 0) + a.n_out - 16, kCheckWeightOffset);
     const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
     if constexpr (F8) return w + (size_t)(wrow0 >> 4) * (nk >> 1) * kFrag;
     return a.packed ? w + (size_t)(wrow0 >> 4) * nk * kFrag : w + (size_t)wrow0 * a.K * 2;
@@ -321,6 +335,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
 
   // paired: issue the weights of 64-k stage P into slot P % S
   auto issue_b64 = [&](const uint8_t* const (&src)[NBL], int P) {
+    BEAM_CHECK(P >= 0 && P < (nk >> 1), kCheckWeightOffset);
     const uint32_t so = (uint32_t)((P % S) * BSTAGE);
     if constexpr (F8) {
 #pragma unroll
@@ -437,6 +452,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   } else {
     // ---- 64-row tiles: 32-k stages, B and A of a stage in one slot ----
     auto issue = [&](int st) {
+      BEAM_CHECK(st >= 0 && st < nk, kCheckWeightOffset);
       const uint32_t so = (uint32_t)((st % S) * SLOT);
 #pragma unroll
       for (int t = 0; t < NBL; ++t)
@@ -616,7 +632,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const uint16_t* __restrict__ W, int64_t w_expert_stride, uint16_t* __restrict__ C,
     const int32_t* __restrict__ plan, int max_tiles, int K, int n_out, int up_row0, int packed,
     const uint16_t* __restrict__ lora_t, const uint16_t* __restrict__ lora_b,
-    int64_t lora_b_stride, int lora_r, const float* __restrict__ scales, int64_t scale_stride) {
+    int64_t lora_b_stride, int lora_r, const float* __restrict__ scales, int64_t scale_stride,
+    int64_t n_rows, int64_t n_src, int n_experts) {
+  (void)n_experts;
   constexpr int WCOLS = (SWIGLU ? kItemBlocks / 2 : kItemBlocks) * 16;
   static_assert(WCOLS == (SWIGLU ? kColsGateUp : kColsDown), "item width is fixed");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[ring_bytes<MB, S, F8>()];
@@ -637,11 +655,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void stream_gemm_kernel(
     const int q = round + xcd * per_xcd + slot;
     if (q >= total) break;
     const int tile = q / nt_n;
-    const int e = plan_expert[tile];
+    const int e = BEAM_CLAMP(plan_expert[tile], 0, n_experts - 1, kCheckPlanRows);
+    BEAM_CHECK(plan_rows[tile] >= 1 && plan_row0[tile] >= 0 &&
+                   (int64_t)plan_row0[tile] + plan_rows[tile] <= n_rows,
+               kCheckPlanRows);
     ItemArgs a{A, gather, topk, W + (size_t)e * w_expert_stride, C, K, n_out, up_row0, packed,
                plan_row0[tile], plan_rows[tile], q - tile * nt_n, lora_t,
                lora_t ? lora_b + (size_t)e * lora_b_stride : nullptr, lora_r, W,
-               w_expert_stride, plan_expert, q, grid, total, nt_n,
+               w_expert_stride, plan_expert, q, grid, total, nt_n, n_rows, n_src,
                F8 ? scales + (size_t)e * scale_stride : nullptr};
     const int nrb = (a.nrows + 15) >> 4;
     gemm_item_dispatch<1, MB, kNW, RG, S, SWIGLU, F8, NT>(nrb, a, lds, wave, lane);
@@ -682,7 +703,10 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t* __restric
       prn[idx] = min(per, n - i * per);
     }
   }
-  if (e == 255) plan[0] = min(sc[255], max_tiles);
+  if (e == 255) {
+    BEAM_CHECK(sc[255] <= max_tiles, kCheckPlanCapacity);
+    plan[0] = min(sc[255], max_tiles);
+  }
 }
 
 // Fragment packing: expert e's [N, K] row-major matrix is rewritten as
@@ -718,8 +742,8 @@ static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int to
                                 const uint16_t* W, int64_t wstride, uint16_t* C,
                                 const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                 int packed, const LoraArgs& lora, int64_t max_items,
-                                hipStream_t stream, const float* scales = nullptr,
-                                int64_t scale_stride = 0) {
+                                hipStream_t stream, const GemmBounds& bounds,
+                                const float* scales = nullptr, int64_t scale_stride = 0) {
   auto kern = stream_gemm_kernel<MB, NW, RG, S, SWIGLU, F8, NT>;
   static int per_cu = 0;  // resident workgroups per CU, fixed per build
   static int cus = 0;
@@ -735,7 +759,8 @@ static hipError_t launch_stream(const uint16_t* A, const int32_t* gather, int to
   const int64_t grid = persistent_grid((int64_t)cus * per_cu, max_items);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), 0, stream, A, gather, topk, W,
                      wstride, C, plan, max_tiles, K, n_out, up_row0, packed, lora.t, lora.b,
-                     lora.b_stride, lora.rank, scales, scale_stride);
+                     lora.b_stride, lora.rank, scales, scale_stride, bounds.n_rows, bounds.n_src,
+                     bounds.n_experts);
   return hipGetLastError();
 }
 
@@ -797,10 +822,10 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                int packed, const LoraArgs& lora, int64_t max_items,
-                               hipStream_t stream, bool stream_weights) {
+                               hipStream_t stream, bool stream_weights, const GemmBounds& bounds) {
 #define BEAM_STREAM_ARGS                                                                    \
   A, gather, topk, W, wstride, C, plan, max_tiles, K, n_out, up_row0, packed, lora, max_items, \
-      stream
+      stream, bounds
 #define BEAM_STREAM_CASE(MBV, NWV, RGV, SV)                                \
   case MBV:                                                                \
     return swiglu ? launch_stream<MBV, NWV, RGV, SV, true>(BEAM_STREAM_ARGS) \
@@ -835,6 +860,8 @@ hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int
 #undef BEAM_STREAM_ARGS
 }
 
+BEAM_DEFINE_CHECK_READER(check_flags_ffn)
+
 // FP8 (E4M3FN) weights through the same 64-k stage pipeline: a weight stage
 // is one 1 KB fragment of 16 rows x 64 k per row block (16 KB per stage),
 // widened to bf16 in registers, and the per-row scales multiply the fp32
@@ -849,7 +876,8 @@ hipError_t launch_grouped_gemm_fp8_paired(int mb, bool swiglu, const uint16_t* A
                                           const int32_t* gather, int topk, const uint8_t* Q,
                                           const float* scales, int64_t qstride, int N, uint16_t* C,
                                           const int32_t* plan, int max_tiles, int K, int n_out,
-                                          int up_row0, int64_t max_items, hipStream_t stream) {
+                                          int up_row0, int64_t max_items, hipStream_t stream,
+                                          const GemmBounds& bounds) {
   const uint16_t* W = reinterpret_cast<const uint16_t*>(Q);
   const int64_t wstride = qstride / 2;  // in 2-byte units: N * K codes per expert
   const LoraArgs none{};
@@ -858,11 +886,11 @@ hipError_t launch_grouped_gemm_fp8_paired(int mb, bool swiglu, const uint16_t* A
     return swiglu ? launch_stream<MBV, 8, 2, SV, true, true>(A, gather, topk, W, wstride, C,    \
                                                              plan, max_tiles, K, n_out,         \
                                                              up_row0, 1, none, max_items,       \
-                                                             stream, scales, N)                 \
+                                                             stream, bounds, scales, N)         \
                   : launch_stream<MBV, 8, 2, SV, false, true>(A, gather, topk, W, wstride, C,   \
                                                               plan, max_tiles, K, n_out,        \
                                                               up_row0, 1, none, max_items,      \
-                                                              stream, scales, N);
+                                                              stream, bounds, scales, N);
   switch (mb) {
     BEAM_FP8P_CASE(8, BEAM_FP8P_S8)
     BEAM_FP8P_CASE(12, BEAM_FP8P_S12)

@@ -391,7 +391,8 @@ int ffn_fp8_choose_mb(int64_t rows, int E) {
 hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                    int topk, const uint8_t* Q, const float* scales, int64_t qstride,
                                    int N, uint16_t* C, const int32_t* plan, int max_tiles, int K,
-                                   int n_out, int up_row0, int64_t max_items, hipStream_t stream) {
+                                   int n_out, int up_row0, int64_t max_items, hipStream_t stream,
+                                   const GemmBounds& bounds) {
 #define BEAM_FP8_CASE(MBV, NWV, RGV, SV)                                                      \
   case MBV:                                                                                     \
     return swiglu ? launch_fp8<MBV, NWV, RGV, SV, true>(A, gather, topk, Q, scales, qstride,  \
@@ -405,7 +406,8 @@ hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const
     case 8:
     case 12:
       return launch_grouped_gemm_fp8_paired(mb, swiglu, A, gather, topk, Q, scales, qstride, N, C,
-                                            plan, max_tiles, K, n_out, up_row0, max_items, stream);
+                                            plan, max_tiles, K, n_out, up_row0, max_items, stream,
+                                            bounds);
     default:
       return hipErrorInvalidValue;
   }

@@ -40,11 +40,18 @@ struct LoraArgs {
   int64_t b_stride = 0;         // elements per expert of b
   int rank = 0;
 };
+// Sizes the checked build verifies indices against (unused otherwise):
+// permuted rows (pairs), rows of A, experts.
+struct GemmBounds {
+  int64_t n_rows = 0;
+  int64_t n_src = 0;
+  int n_experts = 0;
+};
 hipError_t launch_grouped_gemm(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                int topk, const uint16_t* W, int64_t wstride, uint16_t* C,
                                const int32_t* plan, int max_tiles, int K, int n_out, int up_row0,
                                int packed, const LoraArgs& lora, int64_t max_items,
-                               hipStream_t stream, bool stream_weights);
+                               hipStream_t stream, bool stream_weights, const GemmBounds& bounds);
 // whether the gate/up GEMM of a batch of `rows` (token, expert) pairs over E
 // experts loads its weights non-temporally (only the 192-row tiles differ)
 bool ffn_stream_weights(int64_t rows, int E);
@@ -58,16 +65,24 @@ int ffn_fp8_choose_mb(int64_t rows, int E);
 hipError_t launch_grouped_gemm_fp8(int mb, bool swiglu, const uint16_t* A, const int32_t* gather,
                                    int topk, const uint8_t* Q, const float* scales, int64_t qstride,
                                    int N, uint16_t* C, const int32_t* plan, int max_tiles, int K,
-                                   int n_out, int up_row0, int64_t max_items, hipStream_t stream);
+                                   int n_out, int up_row0, int64_t max_items, hipStream_t stream,
+                                   const GemmBounds& bounds);
 // 128/192-row tiles (mb 8 or 12) of the fp8 path, run by the bf16 kernel's
 // 64-k stage pipeline (ffn.hip)
 hipError_t launch_grouped_gemm_fp8_paired(int mb, bool swiglu, const uint16_t* A,
                                           const int32_t* gather, int topk, const uint8_t* Q,
                                           const float* scales, int64_t qstride, int N, uint16_t* C,
                                           const int32_t* plan, int max_tiles, int K, int n_out,
-                                          int up_row0, int64_t max_items, hipStream_t stream);
+                                          int up_row0, int64_t max_items, hipStream_t stream,
+                                          const GemmBounds& bounds);
 hipError_t launch_quantize_fp8(const uint16_t* w, uint8_t* q, float* scales, int E, int N, int K,
                                hipStream_t stream);
+
+// Checked builds: each translation unit's check-flag word, read and cleared
+// (always 0 in the normal build).
+uint32_t check_flags_permute();
+uint32_t check_flags_ffn();
+uint32_t check_flags_combine();
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* perm_dst, const float* w,
                           uint16_t* out, int T, int H, int topk, float scale, hipStream_t stream);

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const uint64_t peers = match_peers(valid ? e : 0, valid);
     if (valid) {
       const uint64_t below = peers & lanemask_lt(lane);
-      const int r = base[e] + __popcll(below);
+      const int r = BEAM_CLAMP(base[e] + __popcll(below), 0, n - 1, kCheckPermuteRow);
       perm_dst[i] = r;
       perm_src[r] = (int32_t)i;
       if (below == 0) base[e] += __popcll(peers);
@@ -158,6 +158,8 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     }
   }
 }
+
+BEAM_DEFINE_CHECK_READER(check_flags_permute)
 
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int32_t* counts, int32_t* offsets,
                           int32_t* perm_src, int32_t* perm_dst, int32_t* chunk_hist,

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "beam_moe.h")).read()
+    import glob
+    text = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
 
 
@@ -23,6 +24,21 @@ def test_library_exports_every_declared_symbol():
     assert declared == sorted(L.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_checked_library_exports_every_declared_symbol():
+    # the debug build with the kernels' index checks has the same ABI
+    lib = L.load(L.LIB_CHECKED_PATH)
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_debug_query_of_the_normal_build():
+    # the normal build has no checks: the query says so without a device
+    f = ctypes.c_uint32(5)
+    assert gtr.lib().moe_debug_check_flags(ctypes.byref(f)) == L.MOE_ERR_UNSUPPORTED
+    assert f.value == 0
+    assert gtr.lib().moe_debug_check_flags(None) == L.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():
