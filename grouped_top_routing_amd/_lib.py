@@ -201,7 +201,12 @@ def _check(t, name, dtype, shape=None, device=None):
 
 
 class Workspace:
-    """A reusable device workspace (a torch uint8 buffer grown on demand)."""
+    """A reusable device workspace (a torch uint8 buffer grown on demand).
+
+    Calls that share one Workspace must be ordered: issue them on one stream,
+    or synchronise between streams yourself.  Each use records the current
+    stream on the buffer, so a buffer replaced when the workspace grows is
+    not reused by torch's allocator before the work queued on it is done."""
 
     def __init__(self):
         self._buf = None
@@ -211,15 +216,19 @@ class Workspace:
             return None
         if self._buf is None or self._buf.numel() < nbytes or self._buf.device != device:
             self._buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self._buf.record_stream(torch.cuda.current_stream(device))
         return self._buf
 
 
+# default workspaces, one per (device, stream): calls on different streams
+# never share scratch memory
 _default_ws: dict = {}
 
 
 def _ws(workspace, device):
     if workspace is None:
-        workspace = _default_ws.setdefault(device, Workspace())
+        key = (device, torch.cuda.current_stream(device).cuda_stream)
+        workspace = _default_ws.setdefault(key, Workspace())
     return workspace
 
 

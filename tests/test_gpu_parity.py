@@ -283,6 +283,29 @@ def test_layer_on_side_stream(tiny):
     assert torch.equal(out, ref)
 
 
+def test_default_workspaces_on_two_streams(tiny):
+    # calls without a workspace on two streams at once: each stream gets its
+    # own default workspace, so the concurrent layers do not share scratch
+    say("[layer] two streams, default workspaces")
+    x1 = synth.make_x(synth.workload("tiny", T=700), 21, DEV)
+    x2 = synth.make_x(synth.workload("tiny", T=300), 22, DEV)
+    args = (tiny["w_router"], tiny["w_gate_up"], tiny["w_down"])
+    r1, r2 = gtr.layer_forward(x1, *args), gtr.layer_forward(x2, *args)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)
+    for _ in range(3):
+        s1.wait_stream(torch.cuda.current_stream(DEV))
+        s2.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.stream(s1):
+            o1 = gtr.layer_forward(x1, *args)
+        with torch.cuda.stream(s2):
+            o2 = gtr.layer_forward(x2, *args)
+        torch.cuda.current_stream(DEV).wait_stream(s1)
+        torch.cuda.current_stream(DEV).wait_stream(s2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, r1) and torch.equal(o2, r2)
+
+
 # ------------------------------------------------------------ packed layout
 def test_pack_weights_is_the_documented_permutation(tiny):
     say("[pack] tiny weights")
