@@ -46,6 +46,7 @@
 #include <stdlib.h>
 
 #include "common.h"
+#include "half_ring.h"
 #include "kernels.h"
 
 namespace beam {
@@ -72,6 +73,33 @@ namespace beam {
 #endif
 #ifndef BEAM_GEMM_DOWN_NT
 #define BEAM_GEMM_DOWN_NT 0
+#endif
+// bf16 weights at 128..256-row tiles: weight ring of half-stage (32-k)
+// slots, A ring of SA 64-k slots, and the weight sub-steps of the next item
+// issued before the epilogue (0: the 64-k stage pipeline instead)
+#ifndef BEAM_GEMM_HALF
+#define BEAM_GEMM_HALF 1
+#endif
+#ifndef BEAM_HALF_SA8
+#define BEAM_HALF_SA8 3
+#endif
+#ifndef BEAM_HALF_SB8
+#define BEAM_HALF_SB8 7
+#endif
+#ifndef BEAM_HALF_SA12
+#define BEAM_HALF_SA12 3
+#endif
+#ifndef BEAM_HALF_SB12
+#define BEAM_HALF_SB12 5
+#endif
+#ifndef BEAM_HALF_SA16
+#define BEAM_HALF_SA16 3
+#endif
+#ifndef BEAM_HALF_SB16
+#define BEAM_HALF_SB16 4
+#endif
+#ifndef BEAM_HALF_KP
+#define BEAM_HALF_KP 2
 #endif
 #ifndef BEAM_GEMM_NW8
 #define BEAM_GEMM_NW8 8
@@ -150,8 +178,21 @@ constexpr int kItemBlocks = 16;
 template <int MB>
 constexpr bool pair_a() { return MB >= 8; }
 __device__ __forceinline__ int a_swizzle(int row) { return (row >> 1) & 7; }
+// bf16 paired tiles with the half-stage weight ring: its slot counts (weight
+// sub-steps SB, A stages SA) and the weight sub-steps issued ahead of an item
+// (KP, at most SB - 1)
+template <int MB, bool F8>
+constexpr bool half_b() { return BEAM_GEMM_HALF && pair_a<MB>() && !F8; }
+template <int MB>
+constexpr int half_sa() { return MB <= 8 ? BEAM_HALF_SA8 : MB <= 12 ? BEAM_HALF_SA12 : BEAM_HALF_SA16; }
+template <int MB>
+constexpr int half_sb() { return MB <= 8 ? BEAM_HALF_SB8 : MB <= 12 ? BEAM_HALF_SB12 : BEAM_HALF_SB16; }
+template <int MB>
+constexpr int half_kp() { return BEAM_HALF_KP < half_sb<MB>() ? BEAM_HALF_KP : half_sb<MB>() - 1; }
 template <int MB, int S, bool F8 = false>
 constexpr int ring_bytes() {
+  if constexpr (half_b<MB, F8>())
+    return (half_sb<MB>() * kItemBlocks + half_sa<MB>() * MB * 2) * kFrag;
   return pair_a<MB>() ? S * (F8 ? 1 : 2) * kItemBlocks * kFrag + 2 * MB * 2 * kFrag
                       : S * (kItemBlocks + MB) * kFrag;
 }
@@ -197,6 +238,23 @@ __device__ __forceinline__ void paired_a_rows(int (&rows)[AM][2], const int32_t*
   }
 }
 
+// Wait of the half-stage pipeline at distance d (D0, D0 + 2, .. DMAX) from
+// the end of the k loop: the count of half_ring::tail_count for this wave's
+// A load count (hi: the larger one); any other d drains.
+template <int SA, int SB, int KP, int NBL, int NA2H, int NA2L, int D, int DMAX>
+__device__ __forceinline__ void wait_half_tail(int d, bool hi) {
+  if constexpr (D > DMAX) {
+    wait_vm<0>();
+  } else {
+    if (d == D) {
+      if (hi) wait_vm<half_ring::tail_count(SA, SB, KP, NBL, NA2H, D)>();
+      else wait_vm<half_ring::tail_count(SA, SB, KP, NBL, NA2L, D)>();
+    } else {
+      wait_half_tail<SA, SB, KP, NBL, NA2H, NA2L, D + 2, DMAX>(d, hi);
+    }
+  }
+}
+
 // One (m-tile, n-tile) item with exactly NRB live 16-row blocks, of which
 // this wave computes RB blocks starting at block row_off.  MB sizes the LDS
 // ring; fragments of blocks NRB..MB-1 are not loaded.
@@ -214,7 +272,11 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   constexpr int BSTAGE = F8 ? BSUB : 2 * BSUB;  // paired: one 64-k weight stage slot
   static_assert(!F8 || kPairA, "fp8 weights run the 64-k stage pipeline only");
   constexpr int APAIR = MB * 2 * kFrag;         // paired: one 64-k A slot
-  constexpr int APOFF = S * BSTAGE;             // paired: A ring after the weight ring
+  // bf16 paired tiles: weight ring of HSB half-stage slots (BSUB each), A ring
+  // of HSA slots
+  constexpr bool kHalfB = half_b<MB, F8>();
+  constexpr int HSA = half_sa<MB>(), HSB = half_sb<MB>(), HKP = half_kp<MB>();
+  constexpr int APOFF = kHalfB ? HSB * BSUB : S * BSTAGE;  // paired: A ring after the weight ring
   static_assert(!kPairA || S >= 3, "a weight stage is issued before the A stage waited with it");
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
   constexpr int WCOLS = CG * HALF * 16;
@@ -222,7 +284,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // Paired: weight stages of the workgroup's next item issued while this
   // item's epilogue runs: S - 2 (the prologue issues stage S - 1 after the
   // first A stages).
-  constexpr int kPre = kPairA ? S - 2 : 0;
+  constexpr int kPre = kHalfB ? HKP : kPairA ? S - 2 : 0;
   // NT: weights are loaded with the non-temporal policy.  The launch picks
   // it where the kernel is a pure weight stream (see launch_grouped_gemm).
   constexpr bool kStreamWeights = NT;
@@ -352,7 +414,144 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     }
   };
 
-  if constexpr (kPairA) {
+  if constexpr (kHalfB) {
+    // ---- bf16, 128..256-row tiles: 32-k weight slots, 64-k A slots ----
+    // The schedule and its wait counts are those of half_ring.h: iteration kt
+    // waits for sub-step kt + 1, passes the barrier, refills A slot
+    // ((kt - 1) / 2) % HSA (odd kt) and weight slot kt % HSB, then reads
+    // sub-step kt + 1's weights while sub-step kt's MFMAs run.  A stages are
+    // issued two stages ahead of their use (HSA = 3), weights HSB - 1
+    // sub-steps ahead.
+    namespace hr = half_ring;
+    const int nst = nk >> 1;  // K is a multiple of 128: nk >= 4
+    // the two per-wave A load counts (na = AMAX or AMAX - 1 blocks)
+    constexpr int NA2H = 2 * AMAX, NA2L = AMAX > 0 ? 2 * (AMAX - 1) : 0;
+    using SH = hr::Steady<HSA, HSB, HKP, NBL, NA2H>;
+    using SL = hr::Steady<HSA, HSB, HKP, NBL, NA2L>;
+    constexpr int kS0 = SH::from > SL::from ? SH::from : SL::from;
+    constexpr int kT = SH::tail > SL::tail ? SH::tail : SL::tail;
+    static_assert(kS0 < 64 && kT < 64, "the schedule reaches a steady state");
+    constexpr int kWOddH = SH::odd, kWOddL = SL::odd, kWEvenH = SH::even, kWEvenL = SL::even;
+    constexpr int kMaxW = SH::max > SL::max ? SH::max : SL::max;
+    static_assert(kMaxW < 64, "vmcnt holds 6 bits");
+    static_assert(SH::ok && SL::ok, "steady counts are safe from sub-step 1 on");
+    constexpr int kDeepMin = SH::deep > SL::deep ? SH::deep : SL::deep;
+    // Waits of the loop (the rule stated in half_ring.h): a loop shorter than
+    // kDeepMin sub-steps drains; otherwise the steady count of the parity of
+    // s, or for the last sub-steps the count at distance d = nk - s from the
+    // end.
+    const bool deep = nk >= kDeepMin;
+
+    auto issue_b = [&](const uint8_t* const (&src)[NBL], int st, uint32_t slot) {
+      BEAM_CHECK(st >= 0 && st < nk, kCheckWeightOffset);
+#pragma unroll
+      for (int t = 0; t < NBL; ++t)
+        lds_dma16_sv<kStreamWeights>(src[t] + (size_t)st * bstep, boff,
+                                     b_base + slot * BSUB + RG * t * kFrag);
+    };
+    auto issue_a = [&](int P, uint32_t slot) {
+      const int k0 = P * 2 * kBKS;
+#pragma unroll
+      for (int j = 0; j < AMAX; ++j)
+        if (j < na) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            lds_dma16(asrc(j, hf, k0), a_base + slot * APAIR + kNW * j * 2 * kFrag + hf * kFrag);
+        }
+    };
+    auto read_b = [&](uint32_t slot, uint4 (&bf)[NCBW]) {
+      const uint8_t* sl = lds + slot * BSUB;
+#pragma unroll
+      for (int cb = 0; cb < NCBW; ++cb)
+        bf[cb] = *reinterpret_cast<const uint4*>(sl + (cg * NCBW + cb) * kFrag + 16 * lane);
+    };
+    // sub-step operand of row block i from A slot `slot`: logical chunk g of
+    // the stage's first 32 k (half 0), 4 + g of the second (bit 6 flipped)
+    auto read_a = [&](uint32_t slot, int half, int i) {
+      const uint8_t* pl = lds + APOFF + slot * APAIR + (aoff0 ^ (half << 6));
+      return *reinterpret_cast<const uint4*>(pl + (row_off + i) * 2 * kFrag);
+    };
+    auto wait_dyn = [&](int s, int last) {
+      wait_vm_dyn<0, kMaxW>(hr::younger_fast(HSA, HSB, HKP, NBL, 2 * na, nk, s, last));
+    };
+    auto next_slot = [](uint32_t x, uint32_t n) { return x + 1 == n ? 0u : x + 1; };
+
+    // Prologue: the front weight sub-steps (unless the previous item issued
+    // them), then what iterations first_iter .. -1 would have issued.
+    if (a.q < a.grid) {
+#pragma unroll
+      for (int st = 0; st < HKP; ++st)
+        if (st < nk) issue_b(bsrc, st, (uint32_t)st);
+    }
+#pragma unroll
+    for (int j = hr::first_iter(HSA, HSB); j < 0; ++j) {
+      if (j % 2 != 0) {
+        const int P = (j - 1) / 2 + HSA;
+        if (P >= 0 && P < nst) issue_a(P, (uint32_t)P);
+      }
+      const int st = j + HSB;
+      if (st >= HKP && st < nk) issue_b(bsrc, st, (uint32_t)st);
+    }
+    wait_dyn(0, -1);
+    stage_barrier();
+    read_b(0u, b0);
+    if constexpr (RB > 0) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) af[i] = read_a(0u, 0, i);
+    }
+    // bs: weight slot of sub-step kt; as: A slot of stage kt / 2
+    uint32_t bs = 0, as = 0;
+    // Sub-steps kt (even) and kt + 1 but the last two.  Away from both ends of
+    // the loop the waits take the counts of a deep loop (immediates); near
+    // them the counts are computed.
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+
+      const uint32_t bs1 = next_slot(bs, HSB), bs2 = next_slot(bs1, HSB);
+      const uint32_t asn = next_slot(as, HSA);
+      // sub-step kt: wait for kt + 1 (odd)
+      if (!deep) wait_vm<0>();
+      else if (kt + 1 + kT < nk) {
+        if (na == AMAX) wait_vm<kWOddH>();
+        else wait_vm<kWOddL>();
+      } else {
+        wait_half_tail<HSA, HSB, HKP, NBL, NA2H, NA2L, 1, kT>(nk - kt - 1, na == AMAX);
+      }
+      wait_lgkm0();     // this wave's reads of sub-step kt's operands have landed
+      stage_barrier();  // sub-step kt + 1 is visible; sub-step kt's slots are free
+      if (kt + HSB < nk) issue_b(bsrc, kt + HSB, bs);
+      read_b(bs1, b1);
+      mfmas(b0, true, [&](int i) { return read_a(as, 1, i); });
+      // sub-step kt + 1: wait for kt + 2 (even, a new A stage)
+      if (!deep) wait_vm<0>();
+      else if (kt + 2 + kT < nk) {
+        if (na == AMAX) wait_vm<kWEvenH>();
+        else wait_vm<kWEvenL>();
+      } else {
+        wait_half_tail<HSA, HSB, HKP, NBL, NA2H, NA2L, 2, kT>(nk - kt - 2, na == AMAX);
+      }
+      wait_lgkm0();
+      stage_barrier();
+      const int P = (kt >> 1) + HSA;
+      if (P < nst) issue_a(P, as);
+      if (kt + 1 + HSB < nk) issue_b(bsrc, kt + 1 + HSB, bs1);
+      read_b(bs2, b0);
+      mfmas(b1, true, [&](int i) { return read_a(asn, 0, i); });
+      bs = bs2;
+      as = asn;
+    }
+    // the last two sub-steps (kt = nk - 2): nothing left to issue
+    if (!deep) wait_vm<0>();
+    else wait_half_tail<HSA, HSB, HKP, NBL, NA2H, NA2L, 1, 1>(1, na == AMAX);
+    wait_lgkm0();
+    stage_barrier();
+    read_b(next_slot(bs, HSB), b1);
+    mfmas(b0, true, [&](int i) { return read_a(as, 1, i); });
+    mfmas(b1, false, [&](int i) { return read_a(as, 1, i); });
+    wait_lgkm0();
+    stage_barrier();  // every wave is done with the ring
+
+  } else if constexpr (kPairA) {
     // ---- 128/192-row tiles: 64-k stages ----
     // Stage P: weights of sub-steps 2P, 2P+1 in slot P % S (issued S - 1
     // stages ahead), A rows in slot P & 1 (issued one stage ahead).  Order of
@@ -549,10 +748,21 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       const uint8_t* nsrc[NBL];
 #pragma unroll
       for (int t = 0; t < NBL; ++t) nsrc[t] = bbase_of(nw, qn - tn * a.nt_n, t);
-      const int nst = a.K / (2 * kBKS);  // the next item's k stages (same K)
+      if constexpr (kHalfB) {
 #pragma unroll
-      for (int P = 0; P < kPre; ++P)
-        if (P < nst) issue_b64(nsrc, P);
+        for (int st = 0; st < kPre; ++st)
+          if (st < nk) {  // the next item's weight sub-steps (same K) into slots 0..kPre-1
+#pragma unroll
+            for (int t = 0; t < NBL; ++t)
+              lds_dma16_sv<kStreamWeights>(nsrc[t] + (size_t)st * bstep, boff,
+                                           b_base + st * BSUB + RG * t * kFrag);
+          }
+      } else {
+        const int nst = a.K / (2 * kBKS);  // the next item's k stages (same K)
+#pragma unroll
+        for (int P = 0; P < kPre; ++P)
+          if (P < nst) issue_b64(nsrc, P);
+      }
     }
   }
 
