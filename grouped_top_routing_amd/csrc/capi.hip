@@ -73,7 +73,7 @@ size_t permute_ws(const moe_config_t* c) {
   return align_up((size_t)(nchunks > 0 ? nchunks : 1) * c->num_experts * sizeof(int32_t));
 }
 size_t plan_bytes(const moe_config_t* c) {
-  return align_up((size_t)(4 + 3 * max_tiles_for(c)) * sizeof(int32_t));
+  return align_up((size_t)plan_ints(max_tiles_for(c)) * sizeof(int32_t));
 }
 size_t ffn_ws(const moe_config_t* c) {
   return plan_bytes(c) + align_up((size_t)pairs(c) * c->intermediate * sizeof(uint16_t));
@@ -145,7 +145,7 @@ int do_permute(const moe_config_t* c, const int32_t* ids, int32_t* counts, int32
 
 int do_plan(const moe_config_t* c, const int32_t* offsets, int32_t* plan, int mb, hipStream_t s) {
   return hip_status(launch_tile_plan(offsets, c->num_experts, ffn_rows_per_tile(mb), plan,
-                                     (int)max_tiles_for(c), s));
+                                     (int)max_tiles_for(c), ffn_blocked_order(mb), s));
 }
 
 // the sizes the checked build verifies the GEMMs' indices against: permuted

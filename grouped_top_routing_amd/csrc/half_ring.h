@@ -25,10 +25,12 @@
 // B sub-step is nbl loads per wave, each A stage na2 loads.
 #pragma once
 
+#ifndef BEAM_HD
 #if defined(__HIPCC__)
 #define BEAM_HD __host__ __device__
 #else
 #define BEAM_HD
+#endif
 #endif
 
 namespace beam {

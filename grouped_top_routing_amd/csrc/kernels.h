@@ -31,8 +31,18 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int32_t* counts,
 int ffn_choose_mb(int64_t rows, int E);
 int ffn_rows_per_tile(int mb);
 int ffn_out_cols_per_item(bool swiglu);
+// The plan (int32): [0] m-tile count, [4 ..] five arrays of max_tiles entries
+// (expert, first row, rows, first m-tile of the tile's expert, m-tiles of the
+// tile's expert), then the round counters of the blocked item order
+// (plan_sync_ints(max_tiles) entries, zeroed by the plan kernel when `sync`).
+constexpr int kPlanSyncPerTile = 32;  // counters per m-tile and GEMM
+constexpr int64_t plan_sync_ints(int64_t max_tiles) { return 2 * kPlanSyncPerTile * max_tiles; }
+constexpr int64_t plan_ints(int64_t max_tiles) { return 4 + 5 * max_tiles + plan_sync_ints(max_tiles); }
 hipError_t launch_tile_plan(const int32_t* offsets, int E, int bmax, int32_t* plan, int max_tiles,
-                            hipStream_t stream);
+                            bool sync, hipStream_t stream);
+// whether the bf16 grouped GEMMs at m-tile height 16 * mb walk their items
+// in the blocked order (and need the plan's round counters zeroed)
+bool ffn_blocked_order(int mb);
 // Expert LoRA second factor for the bf16 expert GEMMs (t == nullptr: none).
 struct LoraArgs {
   const uint16_t* t = nullptr;  // [rows, rank] bf16, scaled first factor
