@@ -87,7 +87,7 @@ def kernel_source_sha256():
     import hashlib
     return hashlib.sha256(b"".join(
         open(os.path.join(ROOT, "grouped_top_routing_amd", "csrc", f), "rb").read()
-        for f in ("ffn.hip", "common.h"))).hexdigest()
+        for f in ("ffn.hip", "common.h", "half_ring.h", "item_order.h"))).hexdigest()
 
 
 def measured_traffic(kernel):
