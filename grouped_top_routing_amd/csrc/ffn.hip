@@ -102,6 +102,19 @@ namespace beam {
 #ifndef BEAM_HALF_KP
 #define BEAM_HALF_KP 2
 #endif
+// refill lag (half_ring.h): 1 drops the per-sub-step wait for the wave's own
+// LDS reads before the barrier, at one sub-step less look-ahead (skewed
+// 16K-token batch at 256-row tiles: 11.52 -> 11.38 ms; prefill at 192-row
+// tiles unchanged, so those keep lag 0 and the deeper look-ahead)
+#ifndef BEAM_HALF_LAG8
+#define BEAM_HALF_LAG8 0
+#endif
+#ifndef BEAM_HALF_LAG12
+#define BEAM_HALF_LAG12 0
+#endif
+#ifndef BEAM_HALF_LAG16
+#define BEAM_HALF_LAG16 1
+#endif
 // 256-row tiles (batches whose experts hold > 160 rows on average): the
 // gate/up GEMM walks its items in expert blocks of 8 m-tiles x 4 n-tiles per
 // XCD and round, and each XCD's workgroups start a round together, so a
@@ -218,6 +231,8 @@ template <int MB>
 constexpr int half_sb() { return MB <= 8 ? BEAM_HALF_SB8 : MB <= 12 ? BEAM_HALF_SB12 : BEAM_HALF_SB16; }
 template <int MB>
 constexpr int half_kp() { return BEAM_HALF_KP < half_sb<MB>() ? BEAM_HALF_KP : half_sb<MB>() - 1; }
+template <int MB>
+constexpr int half_lag() { return MB <= 8 ? BEAM_HALF_LAG8 : MB <= 12 ? BEAM_HALF_LAG12 : BEAM_HALF_LAG16; }
 template <int MB, int S, bool F8 = false>
 constexpr int ring_bytes() {
   if constexpr (half_b<MB, F8>())
@@ -270,16 +285,16 @@ __device__ __forceinline__ void paired_a_rows(int (&rows)[AM][2], const int32_t*
 // Wait of the half-stage pipeline at distance d (D0, D0 + 2, .. DMAX) from
 // the end of the k loop: the count of half_ring::tail_count for this wave's
 // A load count (hi: the larger one); any other d drains.
-template <int SA, int SB, int KP, int NBL, int NA2H, int NA2L, int D, int DMAX>
+template <int SA, int SB, int KP, int LAG, int NBL, int NA2H, int NA2L, int D, int DMAX>
 __device__ __forceinline__ void wait_half_tail(int d, bool hi) {
   if constexpr (D > DMAX) {
     wait_vm<0>();
   } else {
     if (d == D) {
-      if (hi) wait_vm<half_ring::tail_count(SA, SB, KP, NBL, NA2H, D)>();
-      else wait_vm<half_ring::tail_count(SA, SB, KP, NBL, NA2L, D)>();
+      if (hi) wait_vm<half_ring::tail_count(SA, SB, KP, LAG, NBL, NA2H, D)>();
+      else wait_vm<half_ring::tail_count(SA, SB, KP, LAG, NBL, NA2L, D)>();
     } else {
-      wait_half_tail<SA, SB, KP, NBL, NA2H, NA2L, D + 2, DMAX>(d, hi);
+      wait_half_tail<SA, SB, KP, LAG, NBL, NA2H, NA2L, D + 2, DMAX>(d, hi);
     }
   }
 }
@@ -304,7 +319,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   // bf16 paired tiles: weight ring of HSB half-stage slots (BSUB each), A ring
   // of HSA slots
   constexpr bool kHalfB = half_b<MB, F8>();
-  constexpr int HSA = half_sa<MB>(), HSB = half_sb<MB>(), HKP = half_kp<MB>();
+  constexpr int HSA = half_sa<MB>(), HSB = half_sb<MB>(), HKP = half_kp<MB>(), HLAG = half_lag<MB>();
   constexpr int APOFF = kHalfB ? HSB * BSUB : S * BSTAGE;  // paired: A ring after the weight ring
   static_assert(!kPairA || S >= 3, "a weight stage is issued before the A stage waited with it");
   constexpr int HALF = SWIGLU ? NCBW / 2 : NCBW;
@@ -455,8 +470,8 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     const int nst = nk >> 1;  // K is a multiple of 128: nk >= 4
     // the two per-wave A load counts (na = AMAX or AMAX - 1 blocks)
     constexpr int NA2H = 2 * AMAX, NA2L = AMAX > 0 ? 2 * (AMAX - 1) : 0;
-    using SH = hr::Steady<HSA, HSB, HKP, NBL, NA2H>;
-    using SL = hr::Steady<HSA, HSB, HKP, NBL, NA2L>;
+    using SH = hr::Steady<HSA, HSB, HKP, HLAG, NBL, NA2H>;
+    using SL = hr::Steady<HSA, HSB, HKP, HLAG, NBL, NA2L>;
     constexpr int kS0 = SH::from > SL::from ? SH::from : SL::from;
     constexpr int kT = SH::tail > SL::tail ? SH::tail : SL::tail;
     static_assert(kS0 < 64 && kT < 64, "the schedule reaches a steady state");
@@ -464,6 +479,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     constexpr int kMaxW = SH::max > SL::max ? SH::max : SL::max;
     static_assert(kMaxW < 64, "vmcnt holds 6 bits");
     static_assert(SH::ok && SL::ok, "steady counts are safe from sub-step 1 on");
+    static_assert(HLAG == 0 || HLAG == 1, "refill lag");
     constexpr int kDeepMin = SH::deep > SL::deep ? SH::deep : SL::deep;
     // Waits of the loop (the rule stated in half_ring.h): a loop shorter than
     // kDeepMin sub-steps drains; otherwise the steady count of the parity of
@@ -500,20 +516,26 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       const uint8_t* pl = lds + APOFF + slot * APAIR + (aoff0 ^ (half << 6));
       return *reinterpret_cast<const uint4*>(pl + (row_off + i) * 2 * kFrag);
     };
-    auto wait_dyn = [&](int s, int last) {
-      wait_vm_dyn<0, kMaxW>(hr::younger_fast(HSA, HSB, HKP, NBL, 2 * na, nk, s, last));
+    auto wait_dyn = [&](int s) {
+      wait_vm_dyn<0, kMaxW>(hr::younger_fast(HSA, HSB, HKP, NBL, 2 * na, nk, s, hr::last_of(s, HLAG)));
+    };
+    // lag 0: this wave's reads of the operands of the sub-step whose slots
+    // the coming barrier frees must have landed; lag 1 frees older slots
+    auto wait_reads = [&]() {
+      if constexpr (HLAG == 0) wait_lgkm0();
     };
     auto next_slot = [](uint32_t x, uint32_t n) { return x + 1 == n ? 0u : x + 1; };
 
     // Prologue: the front weight sub-steps (unless the previous item issued
-    // them), then what iterations first_iter .. -1 would have issued.
+    // them), then what model iterations first_iter .. -1 - HLAG would have
+    // issued.
     if (a.q < a.grid) {
 #pragma unroll
       for (int st = 0; st < HKP; ++st)
         if (st < nk) issue_b(bsrc, st, (uint32_t)st);
     }
 #pragma unroll
-    for (int j = hr::first_iter(HSA, HSB); j < 0; ++j) {
+    for (int j = hr::first_iter(HSA, HSB); j < -HLAG; ++j) {
       if (j % 2 != 0) {
         const int P = (j - 1) / 2 + HSA;
         if (P >= 0 && P < nst) issue_a(P, (uint32_t)P);
@@ -521,7 +543,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       const int st = j + HSB;
       if (st >= HKP && st < nk) issue_b(bsrc, st, (uint32_t)st);
     }
-    wait_dyn(0, -1);
+    wait_dyn(0);
     stage_barrier();
     read_b(0u, b0);
     if constexpr (RB > 0) {
@@ -535,7 +557,6 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     // them the counts are computed.
     int kt = 0;
     for (; kt + 2 < nk; kt += 2) {
-
       const uint32_t bs1 = next_slot(bs, HSB), bs2 = next_slot(bs1, HSB);
       const uint32_t asn = next_slot(as, HSA);
       // sub-step kt: wait for kt + 1 (odd)
@@ -544,11 +565,20 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
         if (na == AMAX) wait_vm<kWOddH>();
         else wait_vm<kWOddL>();
       } else {
-        wait_half_tail<HSA, HSB, HKP, NBL, NA2H, NA2L, 1, kT>(nk - kt - 1, na == AMAX);
+        wait_half_tail<HSA, HSB, HKP, HLAG, NBL, NA2H, NA2L, 1, kT>(nk - kt - 1, na == AMAX);
       }
-      wait_lgkm0();     // this wave's reads of sub-step kt's operands have landed
-      stage_barrier();  // sub-step kt + 1 is visible; sub-step kt's slots are free
-      if (kt + HSB < nk) issue_b(bsrc, kt + HSB, bs);
+      wait_reads();
+      stage_barrier();  // sub-step kt + 1 is visible; the slots of sub-step kt - HLAG are free
+      if constexpr (HLAG == 0) {
+        // model iteration kt (even): weights only
+        if (kt + HSB < nk) issue_b(bsrc, kt + HSB, bs);
+      } else {
+        // model iteration kt - 1 (odd): A stage kt / 2 - 1 + HSA, then weights
+        const uint32_t bsp = bs == 0 ? HSB - 1 : bs - 1, asp = as == 0 ? HSA - 1 : as - 1;
+        const int P = (kt >> 1) - 1 + HSA;
+        if (P < nst) issue_a(P, asp);
+        if (kt - 1 + HSB < nk) issue_b(bsrc, kt - 1 + HSB, bsp);
+      }
       read_b(bs1, b1);
       mfmas(b0, true, [&](int i) { return read_a(as, 1, i); });
       // sub-step kt + 1: wait for kt + 2 (even, a new A stage)
@@ -557,13 +587,19 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
         if (na == AMAX) wait_vm<kWEvenH>();
         else wait_vm<kWEvenL>();
       } else {
-        wait_half_tail<HSA, HSB, HKP, NBL, NA2H, NA2L, 2, kT>(nk - kt - 2, na == AMAX);
+        wait_half_tail<HSA, HSB, HKP, HLAG, NBL, NA2H, NA2L, 2, kT>(nk - kt - 2, na == AMAX);
       }
-      wait_lgkm0();
+      wait_reads();
       stage_barrier();
-      const int P = (kt >> 1) + HSA;
-      if (P < nst) issue_a(P, as);
-      if (kt + 1 + HSB < nk) issue_b(bsrc, kt + 1 + HSB, bs1);
+      if constexpr (HLAG == 0) {
+        // model iteration kt + 1 (odd): A stage kt / 2 + HSA, then weights
+        const int P = (kt >> 1) + HSA;
+        if (P < nst) issue_a(P, as);
+        if (kt + 1 + HSB < nk) issue_b(bsrc, kt + 1 + HSB, bs1);
+      } else {
+        // model iteration kt (even): weights only
+        if (kt + HSB < nk) issue_b(bsrc, kt + HSB, bs);
+      }
       read_b(bs2, b0);
       mfmas(b1, true, [&](int i) { return read_a(asn, 0, i); });
       bs = bs2;
@@ -571,8 +607,8 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     }
     // the last two sub-steps (kt = nk - 2): nothing left to issue
     if (!deep) wait_vm<0>();
-    else wait_half_tail<HSA, HSB, HKP, NBL, NA2H, NA2L, 1, 1>(1, na == AMAX);
-    wait_lgkm0();
+    else wait_half_tail<HSA, HSB, HKP, HLAG, NBL, NA2H, NA2L, 1, 1>(1, na == AMAX);
+    wait_reads();
     stage_barrier();
     read_b(next_slot(bs, HSB), b1);
     mfmas(b0, true, [&](int i) { return read_a(as, 1, i); });
