@@ -9,6 +9,7 @@ namespace beam {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 // Fourth word of a raw (stride 0, untyped) buffer descriptor on gfx9-family
 // GPUs: DATA_FORMAT = 32 bits (a zero format would make every access out of

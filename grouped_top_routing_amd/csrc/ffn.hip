@@ -126,6 +126,11 @@ namespace beam {
 #ifndef BEAM_GEMM_BLOCKED
 #define BEAM_GEMM_BLOCKED 1
 #endif
+// 16-byte epilogue stores (pairs of column blocks regrouped across lane
+// rows); 0: 8-byte stores
+#ifndef BEAM_EPI_WIDE
+#define BEAM_EPI_WIDE 1
+#endif
 // cache policy bits of the epilogue's stores (0: default)
 #ifndef BEAM_STORE_POLICY_GU
 #define BEAM_STORE_POLICY_GU 0
@@ -851,26 +856,48 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
     // k loop
     int er = r, eg = g;
     asm volatile("" : "+v"(er), "+v"(eg));
+    // the lane's four outputs of row block i, column block j, as bf16 pairs
+    auto outputs = [&](int i, int j) {
+      float o[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (SWIGLU) {
+          const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
+          o[v] = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+        } else {
+          o[v] = acc[i][j][v];
+        }
+      }
+      return u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    };
+    constexpr int kPolicy = SWIGLU ? BEAM_STORE_POLICY_GU : BEAM_STORE_POLICY_DOWN;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int row = (row_off + i) * 16 + er;
+      if constexpr (BEAM_EPI_WIDE && HALF % 2 == 0) {
+        // Column blocks j, j + 1 together: lane rows g = 2m and 2m + 1 (16
+        // lanes each) hold columns 8m..8m+3 and 8m+4..8m+7 of both blocks;
+        // v_permlane16_swap trades block j + 1's half of row 2m for block
+        // j's half of row 2m + 1, so each lane then holds 8 consecutive
+        // columns (row 2m of block j, row 2m + 1 of block j + 1) and writes
+        // them with one 16-byte store: half the store instructions.
 #pragma unroll
-      for (int j = 0; j < HALF; ++j) {
-        float o[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (SWIGLU) {
-            const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
-            o[v] = __fdividef(gt, 1.0f + __expf(-gt)) * up;
-          } else {
-            o[v] = acc[i][j][v];
-          }
+        for (int j = 0; j < HALF; j += 2) {
+          const u32x2_t d0 = outputs(i, j), d1 = outputs(i, j + 1);
+          const auto sx = __builtin_amdgcn_permlane16_swap(d0[0], d1[0], false, false);
+          const auto sy = __builtin_amdgcn_permlane16_swap(d0[1], d1[1], false, false);
+          const int col = a.ntile * WCOLS + cg * HALF * 16 + (j + (eg & 1)) * 16 + 4 * (eg & ~1);
+          const uint32_t off = row < a.nrows ? (uint32_t)(row * a.n_out + col) * 2u : 0x80000000u;
+          const u32x4_t d = {sx[0], sy[0], sx[1], sy[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(d, out, off, 0, kPolicy);
         }
-        const int col = a.ntile * WCOLS + cg * HALF * 16 + j * 16 + 4 * eg;
-        const uint32_t off = row < a.nrows ? (uint32_t)(row * a.n_out + col) * 2u : 0x80000000u;
-        const u32x2_t d = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(d, out, off, 0,
-                                              SWIGLU ? BEAM_STORE_POLICY_GU : BEAM_STORE_POLICY_DOWN);
+      } else {
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+          const int col = a.ntile * WCOLS + cg * HALF * 16 + j * 16 + 4 * eg;
+          const uint32_t off = row < a.nrows ? (uint32_t)(row * a.n_out + col) * 2u : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b64(outputs(i, j), out, off, 0, kPolicy);
+        }
       }
     }
   }
