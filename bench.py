@@ -84,10 +84,18 @@ PROFILE = os.path.join(ROOT, "profiles", "grouped_gemm_prefill_T4096.md")
 
 
 def kernel_source_sha256():
+    """Hash of the grouped GEMM's sources with `//` comments and blank lines
+    removed (comment edits do not change what the counters measured)."""
     import hashlib
-    return hashlib.sha256(b"".join(
-        open(os.path.join(ROOT, "grouped_top_routing_amd", "csrc", f), "rb").read()
-        for f in ("ffn.hip", "common.h", "half_ring.h", "item_order.h"))).hexdigest()
+    import re
+    code = []
+    for f in ("ffn.hip", "common.h", "half_ring.h", "item_order.h"):
+        with open(os.path.join(ROOT, "grouped_top_routing_amd", "csrc", f)) as fh:
+            for line in fh:
+                line = re.sub(r"//.*", "", line).rstrip()
+                if line:
+                    code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def measured_traffic(kernel):

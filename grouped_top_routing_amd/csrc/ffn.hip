@@ -17,10 +17,11 @@
 //
 // * Weights and activations go global -> LDS with gfx950's direct loads
 //   (global_load_lds_dwordx4: 64 lanes x 16 B into 1 KB of LDS, no VGPRs),
-//   through an S-stage ring (stages of 32 k for 64-row tiles, 64 k for
-//   larger ones).  S-1 weight stages are always in flight; each wave waits
-//   on its own vmcnt and one s_barrier per stage publishes the stage to the
-//   other waves.
+//   through rings of LDS slots: 64-row tiles stage 32 k of weights and rows
+//   per slot; bf16 128..256-row tiles keep weights in 32-k slots and rows in
+//   64-k slots (schedule in half_ring.h); fp8 128/192-row tiles run 64-k
+//   stages.  Each wave waits on its own vmcnt and a workgroup barrier
+//   publishes each step to the other waves.
 // * One 1 KB weight "fragment" is exactly one MFMA operand (16 rows x 32 k,
 //   bf16): lane l fetches row l%16, k chunk (l/16)*8, and later reads the
 //   same 16 bytes back with a conflict-free ds_read_b128 at lane*16.  The
@@ -36,8 +37,10 @@
 //   wave-local) for its share of the item's rows (see the work split below).
 // * A persistent grid walks the items.  Workgroup b runs on XCD b % 8; items
 //   are dealt so that the n-tiles of one m-tile land on one XCD in the same
-//   round, sharing the gathered A rows through that XCD's L2.  In the
-//   128/192-row configurations a workgroup issues the first weight stages of
+//   round, sharing the gathered A rows through that XCD's L2 (at 256-row
+//   tiles the gate/up GEMM deals blocks of 8 m-tiles x 4 n-tiles of one
+//   expert instead, item_order.h, and aligns each XCD's rounds).  In the
+//   128..256-row configurations a workgroup issues the first weight loads of
 //   its next item before the current item's epilogue, so its weight stream
 //   keeps running while the outputs are written.
 // * Wave-level values (wave index, wait counts, weight row bases) are kept in
@@ -212,16 +215,17 @@ constexpr int kItemBlocks = 16;
 
 // LDS ring layouts.  64-row tiles: S slots of [16 B fragments | MB A
 // fragments] per 32-k stage, every A fragment a 16-row x 32-k MFMA operand
-// (64 bytes of 16 rows).  128/192-row tiles run 64-k stages (two 32-k MFMA
-// sub-steps, one barrier) so that every A load fetches whole 128-byte lines
-// (the half-line loads cost ~10% at prefill): per 16-row block a stage's A
-// holds 2 KB, rows 0-7 then rows 8-15, each row's 128 bytes with its 16-byte
-// chunks XOR-swizzled by (row / 2) % 8 so that the MFMA operand reads (16
-// rows at one logical chunk) hit distinct LDS banks.  Weights then have a
-// ring of S stage slots of 2 x 16 KB (fp8: 16 KB), issued S - 1 stages
-// ahead, and A a ring of two slots issued one stage ahead (A comes from L2;
-// the weights from HBM need the deeper look-ahead).  Below, "paired" names
-// this 128/192-row family (A staged two MFMA k-steps at a time).
+// (64 bytes of 16 rows).  128..256-row tiles stage A 64 k at a time so that
+// every A load fetches whole 128-byte lines (the half-line loads cost ~10%
+// at prefill): per 16-row block a stage's A holds 2 KB, rows 0-7 then rows
+// 8-15, each row's 128 bytes with its 16-byte chunks XOR-swizzled by
+// (row / 2) % 8 so that the MFMA operand reads (16 rows at one logical
+// chunk) hit distinct LDS banks.  With bf16 weights: a ring of SB 16 KB
+// weight slots, one per 32-k sub-step, then SA A slots (half_ring.h).  With
+// fp8 weights: S 16 KB stage slots of codes (two sub-steps, one barrier),
+// issued S - 1 stages ahead, then two A slots issued one stage ahead.
+// Below, "paired" names this 128..256-row family (A staged two MFMA k-steps
+// at a time).
 template <int MB>
 constexpr bool pair_a() { return MB >= 8; }
 __device__ __forceinline__ int a_swizzle(int row) { return (row >> 1) & 7; }
