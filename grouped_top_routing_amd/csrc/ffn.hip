@@ -470,11 +470,11 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
   if constexpr (kHalfB) {
     // ---- bf16, 128..256-row tiles: 32-k weight slots, 64-k A slots ----
     // The schedule and its wait counts are those of half_ring.h: iteration kt
-    // waits for sub-step kt + 1, passes the barrier, refills A slot
-    // ((kt - 1) / 2) % HSA (odd kt) and weight slot kt % HSB, then reads
-    // sub-step kt + 1's weights while sub-step kt's MFMAs run.  A stages are
-    // issued two stages ahead of their use (HSA = 3), weights HSB - 1
-    // sub-steps ahead.
+    // waits for sub-step kt + 1, passes the barrier, refills the slots of
+    // sub-step j = kt - HLAG (A slot ((j - 1) / 2) % HSA for odd j, weight
+    // slot j % HSB), then reads sub-step kt + 1's weights while sub-step kt's
+    // MFMAs run.  A stages are issued 2 HSA - 2 - HLAG sub-steps ahead of
+    // their use, weights HSB - 1 - HLAG.
     namespace hr = half_ring;
     const int nst = nk >> 1;  // K is a multiple of 128: nk >= 4
     // the two per-wave A load counts (na = AMAX or AMAX - 1 blocks)
