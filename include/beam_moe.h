@@ -208,8 +208,8 @@ int moe_layer_forward(const moe_config_t* cfg, const uint16_t* x, const float* w
  * per GPU it runs on, held until the process ends; the call allocates nothing.
  *   - It serves configurations whose moe_workspace_bytes(MOE_ENTRY_LAYER) is at
  *     most 128 MiB (at the Beam shape, hidden 5120 and intermediate 2560:
- *     batches of up to 512 tokens); larger ones return MOE_ERR_TOO_LARGE and
- *     enqueue nothing.
+ *     batches of up to 1,090 tokens); larger ones return MOE_ERR_TOO_LARGE
+ *     and enqueue nothing.
  *   - It uses the array of the current device; `stream` must belong to it.
  *   - Every call on one GPU shares that GPU's array and leaves its contents
  *     behind: calls that overlap on one GPU (on different streams, or from
