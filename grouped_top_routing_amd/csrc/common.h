@@ -62,6 +62,12 @@ __device__ __forceinline__ float sigmoidf_(float v) {
   return 1.0f / (1.0f + expf(-v));
 }
 
+// SwiGLU product SiLU(g) * u = g * sigmoid(g) * u in FP32, with the library
+// expf and an IEEE divide (no approximate intrinsics)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // ---------------------------------------------------------------------------
 // Checked builds (BEAM_MOE_CHECKED=1, the debug library).  Kernels verify the
 // indices they derive from their inputs before using them; a failing check

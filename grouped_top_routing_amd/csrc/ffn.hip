@@ -867,7 +867,7 @@ __device__ __forceinline__ void gemm_item_rows(const ItemArgs& a, uint8_t* lds, 
       for (int v = 0; v < 4; ++v) {
         if (SWIGLU) {
           const float gt = acc[i][j][v], up = acc[i][j + HALF][v];
-          o[v] = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+          o[v] = silu_mul(gt, up);
         } else {
           o[v] = acc[i][j][v];
         }

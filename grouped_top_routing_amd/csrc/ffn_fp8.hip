@@ -270,7 +270,7 @@ __device__ __forceinline__ void fp8_item_rows(const uint16_t* __restrict__ A,
           float o;
           if (SWIGLU) {
             const float gt = acc[i][j][v] * scale[j], up = acc[i][j + HALF][v] * scale[j + HALF];
-            o = __fdividef(gt, 1.0f + __expf(-gt)) * up;
+            o = silu_mul(gt, up);
           } else {
             o = acc[i][j][v] * scale[j];
           }
