@@ -6,7 +6,8 @@
 // only 8 experts run per token), so the pairs are regrouped expert-major before
 // the expert GEMMs and scattered back after them.
 //
-// Three kernels over fixed chunks of kChunk pairs (one workgroup per chunk,
+// Up to 4096 pairs: one workgroup does all of it (permute_small_kernel).
+// Larger batches: three kernels over fixed chunks of kChunk pairs (one workgroup per chunk,
 // each wave owning a contiguous quarter):
 //   hist     per-wave histograms in LDS; lanes holding the same expert are found
 //            with eight ballots (one per id bit), and only the lowest such lane
@@ -159,11 +160,101 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   }
 }
 
+// Small batches (up to kSmallPairs pairs, e.g. decode): the same stable sort
+// in one workgroup of 16 waves, one launch instead of three.  Wave w owns the
+// contiguous pairs [w q, (w + 1) q) (q a multiple of 64) and holds their ids
+// in registers; its histogram, the scan over experts and the per-wave bases
+// stay in LDS, so the ranks are those of the chunked kernels.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallPerLane = 4;
+constexpr int kSmallPairs = kSmallWaves * 64 * kSmallPerLane;
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids,
+                                                             int n, int E,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm_src,
+                                                             int32_t* __restrict__ perm_dst) {
+  __shared__ int hist[kSmallWaves][kBins];
+  __shared__ int sc[kBins];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kSmallWaves * kBins; i += 1024) (&hist[0][0])[i] = 0;
+  // pairs per wave, a whole number of 64-pair steps (at most kSmallPerLane)
+  const int q = (n + kSmallWaves * 64 - 1) / (kSmallWaves * 64) * 64;
+  const int begin = wave * q, end = min(begin + q, n);
+  int e[kSmallPerLane];
+#pragma unroll
+  for (int j = 0; j < kSmallPerLane; ++j) {
+    const int i = begin + 64 * j + lane;
+    e[j] = 64 * j < q && i < end ? ids[i] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSmallPerLane; ++j) {
+    if (64 * j < q) {  // wave-uniform
+      const bool valid = e[j] >= 0 && e[j] < E;
+      const uint64_t peers = match_peers(valid ? e[j] : 0, valid);
+      if (valid && (peers & lanemask_lt(lane)) == 0) hist[wave][e[j]] += __popcll(peers);
+    }
+  }
+  __syncthreads();
+  // totals per expert, exclusive scan over experts, per-wave first rows
+  int total = 0;
+  if (tid < E)
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) total += hist[w][tid];
+  if (tid < kBins) sc[tid] = tid < E ? total : 0;
+  __syncthreads();
+  for (int off = 1; off < kBins; off <<= 1) {
+    const int v = tid < kBins && tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    if (tid < kBins) sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int excl = sc[tid] - total;
+    counts[tid] = total;
+    offsets[tid] = excl;
+    if (tid == E - 1) offsets[E] = excl + total;
+    int run = excl;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int v = hist[w][tid];
+      hist[w][tid] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int* base = hist[wave];
+#pragma unroll
+  for (int j = 0; j < kSmallPerLane; ++j) {
+    if (64 * j < q) {  // wave-uniform
+      const int i = begin + 64 * j + lane;
+      const bool valid = e[j] >= 0 && e[j] < E;
+      const uint64_t peers = match_peers(valid ? e[j] : 0, valid);
+      if (valid) {
+        const uint64_t below = peers & lanemask_lt(lane);
+        const int r = BEAM_CLAMP(base[e[j]] + __popcll(below), 0, n - 1, kCheckPermuteRow);
+        perm_dst[i] = r;
+        perm_src[r] = i;
+        if (below == 0) base[e[j]] += __popcll(peers);
+      } else if (i < end) {
+        perm_dst[i] = -1;
+      }
+    }
+  }
+}
+
 BEAM_DEFINE_CHECK_READER(check_flags_permute)
 
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int32_t* counts, int32_t* offsets,
                           int32_t* perm_src, int32_t* perm_dst, int32_t* chunk_hist,
                           hipStream_t stream) {
+  if (n > 0 && n <= kSmallPairs) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)n, E,
+                       counts, offsets, perm_src, perm_dst);
+    return hipGetLastError();
+  }
   const int nchunks = (int)((n + kChunk - 1) / kChunk);
   if (nchunks == 0) {
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, stream, chunk_hist, 0, E, counts,

@@ -87,7 +87,10 @@ def test_route_200_tokens():
 
 
 # ------------------------------------------------------------------- permute
-@pytest.mark.parametrize("T,hot", [(1, None), (3, None), (128, None), (513, None), (4097, None),
+# T <= 512 (at most 4096 pairs) runs the one-workgroup kernel, larger batches
+# the chunked kernels; 512 and 513 straddle the boundary
+@pytest.mark.parametrize("T,hot", [(1, None), (3, None), (32, None), (128, None), (512, None),
+                                   (513, None), (4097, None), (500, list(range(40, 48))),
                                    (2000, list(range(100, 108)))])
 def test_permute_exact(T, hot):
     say(f"[permute] T={T} hot={hot is not None}")
@@ -100,16 +103,17 @@ def test_permute_exact(T, hot):
     assert np.array_equal(to_np(pd), rpd)
 
 
-def test_permute_drops_out_of_range_ids():
-    say("[permute] out-of-range ids")
-    ids = _rand_ids(300, seed=5)
+@pytest.mark.parametrize("T", [300, 2000])
+def test_permute_drops_out_of_range_ids(T):
+    say(f"[permute] out-of-range ids T={T}")
+    ids = _rand_ids(T, seed=5)
     ids[3, 2] = -1
     ids[77, 0] = 256
-    ids[299, 7] = 1 << 30
+    ids[T - 1, 7] = 1 << 30
     c, o, ps, pd = gtr.permute(torch.from_numpy(ids).to(DEV))
     rc, ro, rorder, rdst = oracle.permute(ids, 256)
     n = int(ro[-1])
-    assert n == 300 * 8 - 3
+    assert n == T * 8 - 3
     assert np.array_equal(to_np(c), rc) and np.array_equal(to_np(o), ro)
     assert np.array_equal(to_np(ps)[:n], rorder)
     assert np.array_equal(to_np(pd), rdst)
