@@ -7,8 +7,8 @@
 // the expert GEMMs and scattered back after them.
 //
 // Up to 4096 pairs: one workgroup does all of it (permute_small_kernel).
-// Larger batches: three kernels over fixed chunks of kChunk pairs (one workgroup per chunk,
-// each wave owning a contiguous quarter):
+// Larger batches: three kernels over fixed chunks of kChunk pairs (one
+// workgroup per chunk, each wave owning a contiguous quarter):
 //   hist     per-wave histograms in LDS; lanes holding the same expert are found
 //            with eight ballots (one per id bit), and only the lowest such lane
 //            adds the group's size, so no two lanes ever update one counter;
