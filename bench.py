@@ -236,7 +236,7 @@ def expert_host(wts, e):
     return conv(wts["w_gate_up"][e]), conv(wts["w_down"][e])
 
 
-def north_star_stats(y, r):
+def tolerance_stats(y, r):
     """max |y - r| / max(|r|, RMS(r)) and mean |y - r| / RMS(r) (the layer
     output tolerance: 2e-2 and 5e-3)."""
     import numpy as np
@@ -270,7 +270,7 @@ def layer_parity(wl, x, out, ids, wts, sample=None, seed=0):
         gu, dn = expert_host(wts, int(e))
         ref[rows] += wgt[rows, slots][:, None] * oracle.ffn_rows(xn[toks[rows]], gu, dn)
     ref *= 2.5
-    mx, mn = north_star_stats(out.float().cpu().numpy()[toks].astype(np.float64), ref)
+    mx, mn = tolerance_stats(out.float().cpu().numpy()[toks].astype(np.float64), ref)
     return {"tokens": int(T), "output_tokens_compared": int(len(toks)),
             "routing_sets_differing": int((~same).sum()),
             "differing_outside_margin": int((~same & ~flagged).sum()),
@@ -350,7 +350,7 @@ def _parity(ref, rr, gpu_out, gpu_ids, whole, xn, wts):
             gu, dn = expert_host(wts, int(e))
             acc += sc[j] / sc.sum() * oracle.ffn_rows(xn[t:t + 1], gu, dn)[0]
         ref[t] = 2.5 * acc
-    mx, mn = north_star_stats(gpu_out.float().cpu().numpy().astype(np.float64), ref)
+    mx, mn = tolerance_stats(gpu_out.float().cpu().numpy().astype(np.float64), ref)
     return {"tokens": int(gid.shape[0]), "output_tokens_compared": int(gid.shape[0]),
             "routing_sets_differing": int((~same).sum()),
             "differing_outside_margin": int((~same & ~flagged).sum()),
@@ -607,7 +607,7 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, r["x"], wts, args.cpu_experts, torch,
                                               gpu_out=r["out"], gpu_ids=r["ids"])
-    # the benchmark spec layer-output statistics of every workload in one place
+    # the layer-output tolerance statistics of every workload in one place
     par = {}
     if result.get("decode", {}).get("parity"):
         par["decode"] = result["decode"]["parity"]
