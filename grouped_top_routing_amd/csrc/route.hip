@@ -43,8 +43,11 @@ namespace beam {
 // ---------------------------------------------------------------------------
 constexpr int kRT = 128;              // tokens per workgroup
 constexpr int kRB = kRT / 16;         // token row blocks
-constexpr int kRD = 3;                // stages in flight
-constexpr int kRS = kRD + 1;          // LDS ring slots
+// Stages in flight (template parameter kRD): 5 from 4096 tokens up (skewed
+// 16K-token batch: route 174 -> 146 us), 3 below (decode and 512 tokens are
+// 1-2 us slower with 5; the results are the same bits either way).
+constexpr int kRDSmall = 3, kRDLarge = 5;
+constexpr int64_t kRDLargeFrom = 4096;
 constexpr int kRW = 8;                // waves per workgroup
 constexpr int kRC = 256 / kRW / 16;   // 16-expert column blocks per wave
 constexpr int kRL = kRB / kRW + 2 * kRC;  // loads per wave per stage: x fragments + weight halves
@@ -72,14 +75,17 @@ __device__ __forceinline__ void split3(const uint4& w0, const uint4& w1, bf16x8_
   pl = as_bf16x8(L);
 }
 
+template <int kRD>
 __global__ __launch_bounds__(kRW * 64, 1) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ part,
     int T, int H, int kchunk) {
+  constexpr int kRS = kRD + 1;  // LDS ring slots
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kRS * kRB * 1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kRT;
-  const int kbeg = blockIdx.y * kchunk;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int t0 = tile * kRT;
+  const int kbeg = split * kchunk;
   const int nk = kchunk / 32;
 
   // x fragments this wave loads: row blocks wave, wave + kRW, ...
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(kRW * 64, 1) void router_logits_kernel(
     if (kt + j < nk) step(kt + j, wreg[j]);
 
   // D layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column r
-  float* out = part + (size_t)blockIdx.y * T * 256;
+  float* out = part + (size_t)split * T * 256;
 #pragma unroll
   for (int i = 0; i < kRB; ++i)
 #pragma unroll
@@ -314,8 +320,12 @@ __global__ __launch_bounds__(256) void replay_kernel(
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H,
                                 int splits, hipStream_t stream) {
   dim3 grid((T + kRT - 1) / kRT, splits);
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRW * 64), 0, stream, x, wr, part, T, H,
-                     H / splits);
+  if (T >= kRDLargeFrom)
+    hipLaunchKernelGGL(router_logits_kernel<kRDLarge>, grid, dim3(kRW * 64), 0, stream, x, wr,
+                       part, T, H, H / splits);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<kRDSmall>, grid, dim3(kRW * 64), 0, stream, x, wr,
+                       part, T, H, H / splits);
   return hipGetLastError();
 }
 
