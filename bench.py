@@ -3,7 +3,9 @@
 
 One step = one pass of the whole block (router GEMM + sigmoid + group-limited
 top-8, permutation, gate/up grouped GEMM with fused SwiGLU, down grouped GEMM,
-weighted combine x2.5) over one batch of synthetic tokens, through the C ABI.
+weighted combine x2.5) over one batch of synthetic tokens: one call of the C
+ABI's moe_layer_forward.  The same block is also run as its five separate
+calls with HIP events between them, for per-stage and per-kernel times.
 Inputs and all ~20 GB of expert weights are generated on the device before
 timing and stay resident in HBM.
 
@@ -157,6 +159,26 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
                                                       workspace=ws)
         down = lambda h, o: gtr.expert_down(h, o, wd, weight_layout=lay, workspace=ws)
 
+    if fmt == "fp8":
+        layer = lambda: gtr.layer_forward_fp8(x, wr, f8, workspace=ws, return_routing=True)
+    else:
+        layer = lambda: gtr.layer_forward(x, wr, wgu, wd, weight_layout=lay, workspace=ws,
+                                          return_routing=True)
+
+    # The timed step: the whole block as one call of the product's entry point
+    # (moe_layer_forward), `warmup` untimed calls, then `steps` calls bracketed
+    # by synchronisations.
+    for _ in range(warmup):
+        layer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out, ids, topw = layer()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # The same block as its five calls with HIP events between them (on the
+    # stream the library runs on): per-stage and per-kernel times.
     def step(ev=None):
         if ev is not None:
             ev[0].record()
@@ -182,18 +204,21 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(steps):
-        out, ids, counts, topw = step(evs[i])
+        s_out, s_ids, counts, s_topw = step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    staged_wall = time.perf_counter() - t1
+    # both forms compute the same bits
+    assert torch.equal(s_out, out) and torch.equal(s_ids, ids) and torch.equal(s_topw, topw)
+    del s_out, s_ids, s_topw
     names = ["route", "permute", "gate_up", "down", "combine"]
     stage = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
              for j, n in enumerate(names)}
     # device time of each step (first to last event of the step)
     per_step = sorted(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps))
     pct = lambda q: per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
-    # the single-call entry point, for reference, in both weight layouts
+    # the single-call entry point with row-major expert weights, for reference
     def time_layer(a, b, layout):
         for _ in range(2):
             gtr.layer_forward(x, wr, a, b, weight_layout=layout, workspace=ws)
@@ -203,22 +228,11 @@ def run_workload(name, wts, args, steps, warmup, gtr, synth, torch, fmt="bf16", 
             gtr.layer_forward(x, wr, a, b, weight_layout=layout, workspace=ws)
         torch.cuda.synchronize()
         return (time.perf_counter() - t1) * 1e3 / steps
-    if not layer_ref:
-        layer_ms, rowmajor_ms = None, None
-    elif fmt == "fp8":
-        for _ in range(2):
-            gtr.layer_forward_fp8(x, wr, f8, workspace=ws)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(steps):
-            gtr.layer_forward_fp8(x, wr, f8, workspace=ws)
-        torch.cuda.synchronize()
-        layer_ms, rowmajor_ms = (time.perf_counter() - t1) * 1e3 / steps, None
-    else:
-        layer_ms = time_layer(wgu, wd, lay)
-        rowmajor_ms = (None if args.no_row_major_ref or not rowmajor else
-                       time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
-    return {"w": w, "x": x, "ms_per_step": wall * 1e3 / steps, "stage_ms": stage,
+    rowmajor_ms = (None if not layer_ref or fmt == "fp8" or args.no_row_major_ref or not rowmajor
+                   else time_layer(wts["w_gate_up"], wts["w_down"], gtr.LAYOUT_ROW_MAJOR))
+    layer_ms = wall * 1e3 / steps
+    return {"w": w, "x": x, "ms_per_step": layer_ms, "stage_ms": stage,
+            "staged_ms_per_step": staged_wall * 1e3 / steps,
             "device_step_ms": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
             "layer_forward_ms": layer_ms, "row_major_layer_ms": rowmajor_ms,
             "counts": counts.cpu().numpy(), "ids": ids, "out": out, "topw": topw}
@@ -445,6 +459,7 @@ def main():
                   "bf16_mfma_frac": round(mfma_frac, 4), "algorithmic_bytes": alg["layer_bytes"],
                   "expert_flops": alg["expert_flops"], "touched_experts": alg["touched"],
                   "layer_forward_ms": round(r["layer_forward_ms"], 4),
+                  "staged_ms_per_step": round(r["staged_ms_per_step"], 4),
                   "row_major_weights_layer_ms": (None if r["row_major_layer_ms"] is None
                                                  else round(r["row_major_layer_ms"], 4)),
                   "weight_layout": "packed (moe_pack_weights, once at load)",
