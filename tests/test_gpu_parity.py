@@ -103,6 +103,25 @@ def test_permute_exact(T, hot):
     assert np.array_equal(to_np(pd), rpd)
 
 
+@pytest.mark.parametrize("T", [1, 64, 700])
+def test_layer_all_ties_zero_input(tiny, T):
+    """x = 0: every logit is 0 and every score exactly 0.5, so all groups and
+    all experts tie; the lower index wins each tie, giving experts 0..7 (all
+    in group 0) with weights 0.5 / 4 = 0.125, and the output is exactly 0.
+    Both sides reach these values exactly, so they are compared exactly."""
+    say(f"[layer] all-zero input T={T}")
+    x = torch.zeros(T, 256, dtype=torch.bfloat16, device=DEV)
+    out, ids, w = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"],
+                                    return_routing=True)
+    torch.cuda.synchronize()
+    want = np.tile(np.arange(8, dtype=np.int32), (T, 1))
+    assert np.array_equal(to_np(ids), want)
+    assert np.array_equal(to_np(w), np.full((T, 8), 0.125, np.float32))
+    assert not to_np(out).any()
+    rr = oracle.route(to_np(x), tiny["np"]["w_router"])
+    assert np.array_equal(rr.ids, want) and np.all(rr.margin == 0.0)
+
+
 @pytest.mark.parametrize("T", [300, 2000])
 def test_permute_drops_out_of_range_ids(T):
     say(f"[permute] out-of-range ids T={T}")
