@@ -122,6 +122,26 @@ def test_layer_all_ties_zero_input(tiny, T):
     assert np.array_equal(rr.ids, want) and np.all(rr.margin == 0.0)
 
 
+def test_layer_saturated_scores(tiny):
+    """x scaled by 64: logits up to ~90, about 50 experts per token score
+    exactly 1.0 in fp32, and many groups tie at 2.0; every token sits at a
+    selection tie (margin 0), so the GPU's set must be admissible and the
+    output is compared with the oracle evaluated on that set."""
+    say("[layer] saturated sigmoid scores")
+    x = (tiny["x"].float() * 64).to(torch.bfloat16)
+    out, ids, w = gtr.layer_forward(x, tiny["w_router"], tiny["w_gate_up"], tiny["w_down"],
+                                    return_routing=True)
+    torch.cuda.synchronize()
+    npd = tiny["np"]
+    xn = to_np(x)
+    ref = oracle.layer_forward(xn, npd["w_router"], (npd["w_gate_up"], npd["w_down"]))
+    assert (ref["route"].scores == 1.0).sum(axis=1).mean() > 8
+    nf, nd = check_routing(to_np(ids), to_np(w), ref["route"])
+    say(f"  flagged={nf} differing={nd}")
+    assert_close(to_np(out), layer_reference(to_np(ids), ref, xn,
+                                             (npd["w_gate_up"], npd["w_down"])), "out")
+
+
 @pytest.mark.parametrize("T", [300, 2000])
 def test_permute_drops_out_of_range_ids(T):
     say(f"[permute] out-of-range ids T={T}")
