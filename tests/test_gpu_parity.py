@@ -56,6 +56,22 @@ def test_route(tiny, G, KG, K, renorm, bias):
     assert np.all(np.diff(g, axis=1) <= 1e-6)
 
 
+@pytest.mark.parametrize("shift", [-2.0, -0.5])
+def test_route_negative_biased_scores(tiny, shift):
+    """A selection bias that makes the biased scores negative (all of them at
+    -2, about half at -0.5): the kept groups' top-two sums and the expert
+    ranking must treat negative values as values (only ineligible experts are
+    minus infinity); combine weights still come from the unbiased scores."""
+    say(f"[route] negative biased scores, shift {shift}")
+    sb = synth.make_sel_bias(tiny["workload"], 1, device=DEV) + shift
+    ids, w = gtr.route(tiny["x"], tiny["w_router"], sel_bias=sb)
+    torch.cuda.synchronize()
+    rr = oracle.route(tiny["np"]["x"], tiny["np"]["w_router"], sel_bias=to_np(sb))
+    assert (rr.sel < 0).mean() > (0.99 if shift < -1 else 0.2)
+    nf, nd = check_routing(to_np(ids), to_np(w), rr)
+    say(f"  flagged={nf} differing={nd}")
+
+
 def test_route_replay(tiny):
     say("[route_replay] tiny")
     rr = oracle.route(tiny["np"]["x"], tiny["np"]["w_router"])
