@@ -270,7 +270,10 @@ def layer_parity(wl, x, out, ids, wts, sample=None, seed=0):
     import numpy as np
     import oracle
     xn = x.float().cpu().numpy()
-    rr = oracle.route(xn, wts["w_router"].cpu().numpy())
+    wr = wts["w_router"].cpu().numpy()
+    t0 = time.perf_counter()
+    rr = oracle.route(xn, wr)
+    t_route = time.perf_counter() - t0
     gid = ids.cpu().numpy().astype(np.int64)
     same = np.all(np.sort(gid, 1) == np.sort(rr.ids, 1), axis=1)
     flagged = rr.margin < oracle.MARGIN_TOL
@@ -280,17 +283,25 @@ def layer_parity(wl, x, out, ids, wts, sample=None, seed=0):
     s = rr.scores[toks][np.arange(len(toks))[:, None], gid[toks]].astype(np.float64)
     wgt = s / s.sum(axis=1, keepdims=True)
     ref = np.zeros((len(toks), xn.shape[1]))
+    t_ffn = 0.0  # the oracle's expert MLPs and combine, without the weight copies to the host
     for e in np.unique(gid[toks]):
         rows, slots = np.nonzero(gid[toks] == e)
         gu, dn = expert_host(wts, int(e))
+        t0 = time.perf_counter()
         ref[rows] += wgt[rows, slots][:, None] * oracle.ffn_rows(xn[toks[rows]], gu, dn)
+        t_ffn += time.perf_counter() - t0
     ref *= 2.5
     mx, mn = tolerance_stats(out.float().cpu().numpy()[toks].astype(np.float64), ref)
     return {"tokens": int(T), "output_tokens_compared": int(len(toks)),
             "routing_sets_differing": int((~same).sum()),
             "differing_outside_margin": int((~same & ~flagged).sum()),
             "margin_flagged": int(flagged.sum()), "max_rel": mx, "mean_rel": mn,
-            "within_tolerance": bool(mx <= 2e-2 and mn <= 5e-3 and not (~same & ~flagged).any())}
+            "within_tolerance": bool(mx <= 2e-2 and mn <= 5e-3 and not (~same & ~flagged).any()),
+            # the oracle on the host cores: routing of every token, expert MLPs
+            # and combine of the compared tokens
+            "oracle_seconds": {"route_all_tokens": round(t_route, 3),
+                               "expert_mlps_compared_tokens": round(t_ffn, 3),
+                               "cores": os.cpu_count()}}
 
 
 def cpu_baseline(w, x, wts, n_experts, torch, gpu_out=None, gpu_ids=None):

@@ -76,3 +76,29 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_parity_and_cpu_baseline_on_the_oracle_itself():
+    """The benchmark's parity blocks and its CPU baseline, fed the oracle's
+    own bf16-rounded output on the small workload (CPU tensors): no routing
+    difference, errors at the bf16 rounding level, timings recorded."""
+    import torch
+    import oracle
+    import synth
+    d = synth.make_inputs("tiny", 0)
+    w = d["workload"]
+    npw = {k: d[k].float().numpy().astype(np.float64) for k in ("x", "w_router", "w_gate_up",
+                                                                 "w_down")}
+    ref = oracle.layer_forward(npw["x"], npw["w_router"], (npw["w_gate_up"], npw["w_down"]))
+    out = torch.from_numpy(ref["out"]).to(torch.bfloat16)
+    ids = torch.from_numpy(ref["ids"].astype(np.int32))
+    wts = {"w_router": d["w_router"], "w_gate_up": d["w_gate_up"], "w_down": d["w_down"]}
+    p = bench.layer_parity(w, d["x"], out, ids, wts)
+    assert p["routing_sets_differing"] == 0 and p["output_tokens_compared"] == w.T
+    assert p["within_tolerance"] and p["max_rel"] < 1e-2 and p["mean_rel"] < 3e-3
+    assert set(p["oracle_seconds"]) == {"route_all_tokens", "expert_mlps_compared_tokens", "cores"}
+    p = bench.layer_parity(w, d["x"], out, ids, wts, sample=16, seed=1)
+    assert p["output_tokens_compared"] == 16 and p["within_tolerance"]
+    c = bench.cpu_baseline(w, d["x"], wts, 256, torch, gpu_out=out, gpu_ids=ids)
+    assert c["kind"] == "oracle" and c["unit"] == "tokens/s" and c["value"] > 0
+    assert c["parity"]["within_tolerance"] and c["parity"]["routing_sets_differing"] == 0
